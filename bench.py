@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged BF16 KV-cache hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: write the batch's new
+K/V rows into the pool (reshape_and_cache), then paged attention over the
+pool.  Inputs are seeded synthetic BF16 N(0,1) data resident in HBM.
+
+Headline (default --workload decode): B=4 sequences, one query each, KV
+length 7168, Hq 8 / Hkv 2 / Dh 128, 16-token pages permuted at random.  The
+pool holds 40 disjoint page sets (1.17 GB, well above the 256 MB Infinity
+Cache) and step i uses set i % 40, so every step reads K/V from HBM.
+value = decode KV-read bytes per step / step time (GB/s).  The causal
+prefill B=1 Q=KV=4096 Hq 32 / Hkv 8 is measured in the same run and
+reported under "prefill" (TFLOP/s vs the BF16 MFMA peak).
+
+Roofline: the dominant kernel's average duration is timed live with HIP
+events around back-to-back launches on the launch stream; algorithmic bytes
+(or FLOPs) per launch / that duration, against MI355X peaks (HBM 8 TB/s,
+dense BF16 MFMA 2.5 PFLOP/s).  cpu_baseline: the CPU oracle timed on this
+host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "decode KV-read GB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak), µs/call"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- set-up helpers
+
+def to_dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def time_launches(fn, n, stream):
+    """Average GPU time per call of fn() over n back-to-back calls (HIP events on `stream`)."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n * 1e3          # us
+
+
+class DecodeBench:
+    """B=4 x KV7168 decode over S rotating page sets."""
+
+    def __init__(self, sets=40, seed=1235):
+        import torch
+        import paged_kv_cache_bf16_amd as kvp
+        from paged_kv_cache_bf16_amd import workloads as wl
+        self.kvp = kvp
+        self.B, self.L, self.Hq, self.Hkv, self.D = 4, 7168, 8, 2, 128
+        self.S = sets
+        W = self.L // 16
+        rng = np.random.default_rng(seed)
+        nb = sets * self.B * W
+        bt = rng.permutation(nb).astype(np.int32).reshape(sets * self.B, W)
+        self.pool = kvp.alloc_pool(nb, self.Hkv, self.D, interleaved=False)
+        # fill every page with seeded N(0,1) BF16 through reshape_and_cache, one set at a time
+        gen = torch.Generator(device="cuda").manual_seed(seed)
+        self.sl = torch.full((self.B,), self.L, dtype=torch.int32, device="cuda")
+        self.qsl = torch.arange(self.B + 1, dtype=torch.int32, device="cuda")
+        self.bt, self.q, self.knew, self.vnew, self.slot_new = [], [], [], [], []
+        pos = np.arange(self.L, dtype=np.int64)
+        for s in range(sets):
+            rows = bt[s * self.B:(s + 1) * self.B]
+            slots = np.concatenate([rows[b, pos // 16].astype(np.int64) * 16 + pos % 16 for b in range(self.B)])
+            T = slots.shape[0]
+            k = torch.randn(T, self.Hkv, self.D, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+            v = torch.randn(T, self.Hkv, self.D, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+            sd = torch.from_numpy(slots).cuda()
+            kvp.reshape_and_cache(self.pool, k, v, sd)
+            last = torch.arange(self.B, device="cuda") * self.L + self.L - 1
+            self.knew.append(k[last].contiguous())
+            self.vnew.append(v[last].contiguous())
+            self.slot_new.append(sd[last].contiguous())
+            self.bt.append(torch.from_numpy(kvp.kv_prepare_block_tables(self.pool, rows, [self.L] * self.B)).cuda())
+            self.q.append(torch.randn(self.B, self.Hq, self.D, generator=gen, device="cuda")
+                          .to(torch.bfloat16).view(torch.int16))
+            if s == 0:
+                self.host0 = dict(k=k.cpu().numpy().view(np.uint16), v=v.cpu().numpy().view(np.uint16),
+                                  slots=slots, bt=rows.copy(), q=self.q[0].cpu().numpy().view(np.uint16))
+            del k, v
+        self.out = torch.zeros(self.B, self.Hq, self.D, dtype=torch.int16, device="cuda")
+        self.ws = kvp.alloc_workspace(self.pool, self.Hq, self.B, self.L)
+        self.scale = 1.0 / math.sqrt(self.D)
+        self.i = 0
+        torch.cuda.synchronize()
+
+    @property
+    def kv_bytes(self):
+        return self.B * self.L * self.Hkv * self.D * 2 * 2
+
+    @property
+    def algo_bytes(self):
+        # K/V read + q read + out write + active block-table entries
+        return self.kv_bytes + 2 * self.B * self.Hq * self.D * 2 + self.B * (self.L // 16) * 4
+
+    def attention(self, s):
+        self.kvp.paged_attention(self.pool, self.q[s], self.out, self.Hq, self.bt[s], self.sl, self.qsl, 1, self.L,
+                                 self.scale, True, workspace=self.ws)
+
+    def step(self):
+        s = self.i % self.S
+        self.i += 1
+        self.kvp.reshape_and_cache(self.pool, self.knew[s], self.vnew[s], self.slot_new[s])
+        self.attention(s)
+
+    def attention_only(self):
+        s = self.i % self.S
+        self.i += 1
+        self.attention(s)
+
+    def check_against_oracle(self):
+        """Set 0 output vs the oracle (tolerance), so the timed path is a correct one."""
+        import oracle
+        h = self.host0
+        self.attention(0)
+        import torch
+        torch.cuda.synchronize()
+        got = oracle.bf16_bits_to_f32(self.out.cpu().numpy().view(np.uint16))
+        pool = oracle.Pool(self.S * self.B * (self.L // 16), self.Hkv, self.D)
+        oracle.reshape_and_cache(pool, h["k"], h["v"], h["slots"])
+        ref = oracle.paged_attention(h["q"], pool, h["bt"], [self.L] * self.B, np.arange(self.B + 1),
+                                     self.Hq, self.scale, True)
+        err = np.abs(got.astype(np.float64) - ref)
+        return float(err.max()), float(err.mean()), pool, ref
+
+    def cpu_baseline(self, pool, budget_s=10.0):
+        import oracle
+        h = self.host0
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.paged_attention(h["q"], pool, h["bt"], [self.L] * self.B, np.arange(self.B + 1), self.Hq,
+                                   self.scale, True)
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = (time.perf_counter() - t0) / n
+        threads = min(_omp_threads(), self.B)
+        return {"value": round(self.algo_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+                "kind": "oracle",
+                "sample": "%d full decode calls (B4 KV7168, all 8 heads) in %.1f s, %.1f ms/call; the oracle "
+                          "parallelises over query rows, so %d threads were busy" % (n, n * dt, dt * 1e3, threads)}
+
+
+class PrefillBench:
+    """Causal prefill B=1, Q=KV=4096, Hq 32 / Hkv 8, Dh 128, reversed pages."""
+
+    def __init__(self, seed=1236):
+        import torch
+        import paged_kv_cache_bf16_amd as kvp
+        from paged_kv_cache_bf16_amd import workloads as wl
+        self.kvp = kvp
+        self.w = w = wl.prefill()
+        self.pool = kvp.alloc_pool(w.num_blocks, w.num_kv_heads, w.head_dim)
+        self.k, self.v = to_dev(w.k), to_dev(w.v)
+        self.slots = torch.from_numpy(w.slot_mapping).cuda()
+        kvp.reshape_and_cache(self.pool, self.k, self.v, self.slots)
+        self.bt = torch.from_numpy(kvp.kv_prepare_block_tables(self.pool, w.block_tables, w.seq_lens)).cuda()
+        self.sl = torch.from_numpy(w.seq_lens).cuda()
+        self.qsl = torch.from_numpy(w.query_start_loc).cuda()
+        self.q = to_dev(w.q)
+        self.out = torch.zeros_like(self.q)
+        self.L = int(w.seq_lens[0])
+        torch.cuda.synchronize()
+
+    @property
+    def flops(self):
+        w = self.w
+        return 4.0 * w.head_dim * w.num_q_heads * (self.L * (self.L + 1) / 2)
+
+    def attention(self):
+        w = self.w
+        self.kvp.paged_attention(self.pool, self.q, self.out, w.num_q_heads, self.bt, self.sl, self.qsl, self.L,
+                                 self.L, w.scale, True)
+
+    def step(self):
+        self.kvp.reshape_and_cache(self.pool, self.k, self.v, self.slots)
+        self.attention()
+
+
+def _omp_threads():
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    return min(aff, int(env)) if env and env.isdigit() else aff
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1400)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--sets", type=int, default=40, help="rotating decode page sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the pool lives on one device); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_bf16_amd as kvp
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    log("setting up decode workload (%d page sets)" % args.sets)
+    dec = DecodeBench(sets=args.sets)
+    log("decode set-up done; checking against the oracle")
+    mx, mean, opool, _ = dec.check_against_oracle()
+    log("decode parity: max_abs=%.3g mean_abs=%.3g" % (mx, mean))
+    assert mx <= 2e-2 and mean <= 2e-3, "decode output out of tolerance"
+
+    for _ in range(args.warmup):
+        dec.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        dec.step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    log("decode: %.2f us/step (wall %.2f us/step)" % (ms_step * 1e3, wall / args.steps * 1e6))
+
+    # dominant kernel alone: 7 groups x 200 back-to-back launches, median
+    groups = [time_launches(dec.attention_only, 200, stream) for _ in range(7)]
+    attn_us = float(np.median(groups))
+    log("decode attention: %.2f us/call (groups %s)" % (attn_us, ["%.2f" % g for g in groups]))
+    # the same with the pool warm in the Infinity Cache (one page set)
+    warm_us = time_launches(lambda: dec.attention(0), 400, stream)
+
+    c0 = kvp.kvp_get_counters()
+    assert c0["split_kv_launches"] > 0
+
+    result = {
+        "metric": METRIC,
+        "value": round(dec.algo_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode B4 Q1 KV7168 Hq8 Hkv2 Dh128 page16 (random page permutation), "
+                               "%d rotating page sets over a %.2f GB pool; step = reshape_and_cache of the 4 new "
+                               "tokens + split-KV decode" % (dec.S, dec.S * dec.kv_bytes / 1e9),
+                   "global_batch": dec.B, "seq_len": dec.L, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(dec.algo_bytes / (attn_us * 1e-6) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec.algo_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "split_kv_kernel<128>", "us_per_call": round(attn_us, 3),
+                     "algo_bytes_per_call": dec.algo_bytes},
+        "decode_warm_cache": {"us_per_call": round(warm_us, 3),
+                              "GBps": round(dec.algo_bytes / (warm_us * 1e-6) / 1e9, 1)},
+        "parity": {"decode_max_abs": mx, "decode_mean_abs": mean},
+        "context": "the pages report 0.272859 ms for B4 Q1 KV7168 paged attention on MI300X (head counts not "
+                   "given); not comparable as a target",
+    }
+
+    if not args.no_prefill:
+        log("setting up prefill workload")
+        pre = PrefillBench()
+        for _ in range(3):
+            pre.step()
+        torch.cuda.synchronize()
+        step_us = time_launches(pre.step, 20, stream)
+        pgroups = [time_launches(pre.attention, 20, stream) for _ in range(5)]
+        p_us = float(np.median(pgroups))
+        tf = pre.flops / (p_us * 1e-6) / 1e12
+        result["prefill"] = {"workload": "causal prefill B1 Q4096 KV4096 Hq32 Hkv8 Dh128 page16 reversed pages",
+                             "us_per_call": round(p_us, 2), "us_per_step_with_cache_write": round(step_us, 2),
+                             "TFLOPs": round(tf, 2), "peak_TFLOPs": BF16_PEAK_TFLOPS,
+                             "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops_per_call": pre.flops,
+                             "kernel": "prefill_kernel<128,2>"}
+        log("prefill: %.2f us/call, %.1f TFLOP/s" % (p_us, tf))
+        del pre
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = dec.cpu_baseline(opool, budget_s=args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

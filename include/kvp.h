@@ -1,0 +1,205 @@
+/*
+ * kvp.h -- C ABI of the MI355X (gfx950) paged BF16 KV-cache library.
+ *
+ * The library implements the composition described on the pages
+ *   "test(rocm): ReshapeAndCache->PagedAttention composition at real dims"
+ *     (What changed; review thread: the slot of logical token i of a
+ *     sequence is block_table[i / 16] * 16 + i % 16) and
+ *   "fix(rocm): stabilize direct paged CK attention for bitwise R/R"
+ *     (Changes: one fixed arithmetic schedule so that prefill and decode give
+ *     the same BF16 bits; padded and sanitised tail page tables; 64-bit
+ *     addressing for pools over 2 GB; no dense KV materialisation),
+ * i.e. a cache scatter (reshape_and_cache) followed by GQA attention that
+ * reads K/V in place through per-sequence block tables (paged_attention),
+ * for causal prefill, suffix prefill and single-query decode.
+ *
+ * Conventions shared by every entry point
+ *   - Every function returns an int: KVP_OK (0) or a negative KVP_ERR_*.
+ *     All argument checks run before anything is submitted to the GPU; a
+ *     call that returns an error has queued no work, written no memory and
+ *     left the current HIP device unchanged.  kvp_last_error() then
+ *     describes the failure (thread-local, valid until the next call on the
+ *     same thread).  After submission a HIP failure returns KVP_ERR_HIP; it
+ *     is never retried and no other path is tried instead.
+ *   - Device buffers (pool, q, k, v, out, tables, workspace) are owned by the
+ *     caller.  The library owns only the small host-side pool descriptor and
+ *     never allocates device memory.
+ *   - Work is queued on the caller's stream (a hipStream_t passed as void*;
+ *     NULL is the default stream).  No entry point synchronises the host.
+ *   - BF16 values are passed as raw 16-bit patterns (uint16_t storage).
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef KVP_H
+#define KVP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVP_BLOCK_SIZE 16           /* tokens per page (block) */
+
+enum {
+    KVP_OK = 0,
+    KVP_ERR_INVALID_ARGUMENT = -1,  /* null pointer, bad size, inconsistent metadata */
+    KVP_ERR_UNSUPPORTED = -2,       /* head_dim not 128/256/512, block_size != 16, Hq % Hkv != 0, G > 16 */
+    KVP_ERR_WORKSPACE_TOO_SMALL = -3,
+    KVP_ERR_HIP = -4                /* a HIP call failed after validation */
+};
+
+/*
+ * KV pool layout (one page = 16 tokens of one kv head of one block):
+ *   K page: [head_dim / 8][16 tokens][8 dims]  BF16  (16-byte dim groups, token-major inside)
+ *   V page: [head_dim][16 tokens]              BF16  (dim-major: each dim's 16 tokens contiguous)
+ *   element (block b, kv head h, token t, dim d):
+ *     K: k_cache[b * k_block_stride + h * 16 * head_dim + (d / 8) * 128 + t * 8 + d % 8]
+ *     V: v_cache[b * v_block_stride + h * 16 * head_dim + d * 16 + t]
+ * Strides are in elements and must be >= num_kv_heads * 16 * head_dim.
+ * Separate pools: k_cache, v_cache distinct; both strides = Hkv * 16 * head_dim.
+ * Interleaved pool: one allocation, v_cache = k_cache + Hkv * 16 * head_dim,
+ * both strides = 2 * Hkv * 16 * head_dim (each block: K pages then V pages).
+ * Block addresses are always formed in 64-bit arithmetic, so pools larger
+ * than 2 GB (or 4 GB) are addressed correctly.  Pointers must be 16-byte
+ * aligned.
+ */
+typedef struct {
+    int64_t num_blocks;
+    int32_t block_size;             /* must be KVP_BLOCK_SIZE */
+    int32_t num_kv_heads;
+    int32_t head_dim;               /* 128, 256 or 512 */
+    int32_t reserved;
+    void *k_cache;                  /* device, caller-owned */
+    void *v_cache;                  /* device, caller-owned */
+    int64_t k_block_stride;         /* elements */
+    int64_t v_block_stride;         /* elements */
+} kvp_pool_desc;
+
+typedef struct kvp_pool kvp_pool;   /* opaque host-side descriptor */
+
+/* Validate desc and create a descriptor.  *out receives the handle.
+ * Errors: INVALID_ARGUMENT (null, non-positive sizes, short strides,
+ * misaligned pointers, overlapping K/V pages), UNSUPPORTED (head_dim,
+ * block_size). */
+int kv_pool_create(const kvp_pool_desc *desc, kvp_pool **out);
+
+/* Release a descriptor (the caller's device memory is untouched). */
+int kv_pool_destroy(kvp_pool *pool);
+
+/* Total bytes spanned by the pool from its lowest to highest page byte
+ * (what decides whether 32-bit offsets would overflow). */
+int kv_pool_span_bytes(const kvp_pool *pool, int64_t *bytes);
+
+/*
+ * reshape_and_cache -- scatter new K/V rows into the pool
+ * ("test(rocm): ReshapeAndCache->PagedAttention composition at real dims",
+ * What changed).  For each token i in [0, num_tokens) with
+ * s = slot_mapping[i] >= 0, copies the bits of k[i][h][:] and v[i][h][:]
+ * (h < num_kv_heads) into block s / 16, token s % 16.  Nothing else in the
+ * pool changes.  Negative slots are skipped.
+ *   k, v          device, [num_tokens][num_kv_heads][head_dim] BF16 with
+ *                 token strides k_token_stride / v_token_stride (elements,
+ *                 >= num_kv_heads * head_dim); heads and dims contiguous.
+ *   slot_mapping  device, [num_tokens] int64.
+ * Preconditions not checked on the device: no two tokens share a slot (the
+ * result would be one of them), every slot < num_blocks * 16 (larger slots
+ * are skipped by the kernel).
+ */
+int reshape_and_cache(const kvp_pool *pool, const void *k, const void *v, int64_t num_tokens,
+                      int64_t k_token_stride, int64_t v_token_stride,
+                      const int64_t *slot_mapping, void *stream);
+
+/*
+ * kv_prepare_block_tables -- page-table metadata prep, host only
+ * ("fix(rocm): stabilize direct paged CK attention for bitwise R/R",
+ * Changes: pad page tables to complete KV tiles and sanitise unused
+ * columns of active and inactive rows).
+ *   block_tables  host, [num_seqs][width] int32 (raw; columns past a row's
+ *                 last page may hold anything)
+ *   seq_lens      host, [num_seqs] int32, >= 0 (0 = inactive row)
+ *   out           host, [num_seqs][kvp_padded_width(width)] int32
+ * Columns < ceil(seq_len / 16) must name blocks in [0, num_blocks); they are
+ * copied.  Every other column becomes the row's last valid block, or 0 for a
+ * row without pages.  The caller copies `out` to the device and passes it to
+ * paged_attention with stride kvp_padded_width(width).
+ * Errors: INVALID_ARGUMENT (a row needs more than `width` pages, an active
+ * entry is out of range, negative seq_len); `out` is then untouched.
+ */
+int kv_prepare_block_tables(const kvp_pool *pool, const int32_t *block_tables, int32_t num_seqs,
+                            int32_t width, const int32_t *seq_lens, int32_t *out);
+
+/* Width a prepared table has: width rounded up to a multiple of 8 pages. */
+int32_t kvp_padded_width(int32_t width);
+
+/*
+ * Bytes of device workspace paged_attention needs for these bounds.  The
+ * workspace holds per-tile partial softmax states of the split-KV path and
+ * one ticket counter per (sequence, kv head).  Its counters must be zero
+ * before the first call (kvp_workspace_init does that); every call leaves
+ * them zero again.  One workspace must not be used by two calls that can
+ * run at the same time.
+ */
+int kvp_workspace_bytes(const kvp_pool *pool, int32_t num_q_heads, int32_t num_seqs,
+                        int32_t max_seq_len, size_t *bytes);
+
+/* Zero a workspace's counters on `stream` with a fill kernel. */
+int kvp_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention -- GQA attention reading K/V in place through block tables
+ * ("fix(rocm): stabilize direct paged CK attention for bitwise R/R",
+ * Changes and Additional checks; the decode request-to-query mapping uses
+ * one query per row).
+ *   q     device, [total_q][num_q_heads][head_dim] BF16, token stride
+ *         q_token_stride (elements); total_q = query_start_loc[num_seqs].
+ *   out   device, same shape, token stride out_token_stride.
+ *   block_tables     device, [num_seqs][block_table_stride] int32, as made
+ *                    by kv_prepare_block_tables (block_table_stride >=
+ *                    ceil(max_seq_len / 16)).
+ *   seq_lens         device, [num_seqs] int32: KV length of each row.
+ *   query_start_loc  device, [num_seqs + 1] int32: row b's queries are
+ *                    q[query_start_loc[b] .. query_start_loc[b+1]); they sit
+ *                    at the last q_len positions of the row (bottom-right).
+ *   max_query_len, max_seq_len  host bounds of the device metadata (no sync).
+ *   scale            softmax scale applied to q.k.
+ *   causal           1: query at position p sees keys 0..p; 0: all keys.
+ * Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ * Rows with q_len == 0 are skipped; rows that violate 0 <= q_len <=
+ * seq_len <= max_seq_len produce no output and no memory access.
+ * Numerics: one fixed arithmetic schedule (KV tiles and their softmax folds
+ * at fixed absolute positions), so an output row's bits do not depend on
+ * the batch, the other rows, the query count or the kernel chosen: a decode
+ * call gives bitwise the same row as the prefill that ends at that token.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP.
+ */
+int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride, void *out,
+                    int64_t out_token_stride, int32_t num_q_heads, int32_t num_seqs,
+                    const int32_t *block_tables, int32_t block_table_stride,
+                    const int32_t *seq_lens, const int32_t *query_start_loc,
+                    int32_t max_query_len, int32_t max_seq_len, float scale, int causal,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Dispatch counters: evidence of which kernel actually ran. */
+typedef struct {
+    uint64_t reshape_and_cache_launches;
+    uint64_t split_kv_launches;        /* decode / short-query kernel */
+    uint64_t prefill_launches;         /* streaming prefill kernel */
+    uint64_t workspace_init_launches;
+    uint64_t last_grid_blocks;         /* workgroups of the most recent launch */
+} kvp_counters;
+
+int kvp_get_counters(kvp_counters *out);
+int kvp_reset_counters(void);
+
+/* Thread-local description of the last error ("" after success). */
+const char *kvp_last_error(void);
+
+/* Library version string. */
+const char *kvp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVP_H */

@@ -1,0 +1,353 @@
+// C-ABI entry points: argument validation, page-table preparation, workspace
+// sizing, kernel dispatch and dispatch counters.  Every check runs before the
+// first launch, so a rejected call queues nothing and writes nothing; the
+// library never changes the current HIP device and never allocates device
+// memory.  The error policy follows "ROCm: harden compact peer-local KV
+// prefill for Gemma-4" (Required hardening: failures before submission leave
+// state unchanged; after submission a failure is reported, never retried or
+// routed elsewhere).
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "kvp_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+std::atomic<uint64_t> g_cache_launches{0}, g_split_launches{0}, g_prefill_launches{0},
+    g_init_launches{0}, g_last_grid{0};
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok()
+{
+    g_err.clear();
+    return KVP_OK;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(KVP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t page_elems(const kvp_pool_desc &d) { return (int64_t)d.num_kv_heads * KVP_BLOCK_SIZE * d.head_dim; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+int kv_pool_create(const kvp_pool_desc *desc, kvp_pool **out)
+{
+    if (!desc || !out)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: null argument");
+    const kvp_pool_desc &d = *desc;
+    if (d.block_size != KVP_BLOCK_SIZE)
+        return fail(KVP_ERR_UNSUPPORTED, "kv_pool_create: block_size %d (only %d)", d.block_size, KVP_BLOCK_SIZE);
+    if (d.head_dim != 128 && d.head_dim != 256 && d.head_dim != 512)
+        return fail(KVP_ERR_UNSUPPORTED, "kv_pool_create: head_dim %d (128, 256, 512)", d.head_dim);
+    if (d.num_blocks <= 0 || d.num_kv_heads <= 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: num_blocks and num_kv_heads must be positive");
+    if (!d.k_cache || !d.v_cache)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: null cache pointer");
+    if (!aligned16(d.k_cache) || !aligned16(d.v_cache))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: cache pointers must be 16-byte aligned");
+    const int64_t pg = page_elems(d);
+    if (d.k_block_stride < pg || d.v_block_stride < pg)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: block strides must be >= %lld elements", (long long)pg);
+    if (d.k_block_stride % 8 || d.v_block_stride % 8)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: block strides must be multiples of 8 elements");
+    // K and V page sets of the same block index must not overlap, and with
+    // equal strides the two lattices must interleave without touching.
+    const int64_t diff = ((const char *)d.v_cache - (const char *)d.k_cache) / 2;
+    if (d.k_block_stride == d.v_block_stride) {
+        const int64_t s = d.k_block_stride;
+        int64_t r = diff % s;
+        if (r < 0)
+            r += s;
+        const bool far = diff >= d.num_blocks * s || -diff >= d.num_blocks * s;
+        if (!far && (r < pg || s - r < pg))
+            return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: K and V pages overlap");
+    }
+    kvp_pool *p = new (std::nothrow) kvp_pool;
+    if (!p)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: out of host memory");
+    p->d = d;
+    *out = p;
+    return ok();
+}
+
+int kv_pool_destroy(kvp_pool *pool)
+{
+    delete pool;
+    return ok();
+}
+
+int kv_pool_span_bytes(const kvp_pool *pool, int64_t *bytes)
+{
+    if (!pool || !bytes)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_span_bytes: null argument");
+    const kvp_pool_desc &d = pool->d;
+    const int64_t pg = page_elems(d);
+    const char *k0 = (const char *)d.k_cache, *v0 = (const char *)d.v_cache;
+    const char *k1 = k0 + 2 * ((d.num_blocks - 1) * d.k_block_stride + pg);
+    const char *v1 = v0 + 2 * ((d.num_blocks - 1) * d.v_block_stride + pg);
+    const char *lo = k0 < v0 ? k0 : v0;
+    const char *hi = k1 > v1 ? k1 : v1;
+    *bytes = (int64_t)(hi - lo);
+    return ok();
+}
+
+int reshape_and_cache(const kvp_pool *pool, const void *k, const void *v, int64_t num_tokens,
+                      int64_t k_token_stride, int64_t v_token_stride, const int64_t *slot_mapping,
+                      void *stream)
+{
+    if (!pool)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: null pool");
+    const kvp_pool_desc &d = pool->d;
+    if (num_tokens < 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: negative num_tokens");
+    if (num_tokens == 0)
+        return ok();
+    if (!k || !v || !slot_mapping)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: null pointer");
+    if (!aligned16(k) || !aligned16(v))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: k and v must be 16-byte aligned");
+    const int64_t row = (int64_t)d.num_kv_heads * d.head_dim;
+    if (k_token_stride < row || v_token_stride < row || k_token_stride % 8 || v_token_stride % 8)
+        return fail(KVP_ERR_INVALID_ARGUMENT,
+                    "reshape_and_cache: token strides must be >= %lld and multiples of 8", (long long)row);
+    if (num_tokens > ((int64_t)1 << 40) / row)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: num_tokens too large");
+    kvp::CacheArgs a;
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.num_tokens = num_tokens;
+    a.k_token_stride = k_token_stride;
+    a.v_token_stride = v_token_stride;
+    a.slot_mapping = slot_mapping;
+    a.k_cache = (uint16_t *)d.k_cache;
+    a.v_cache = (uint16_t *)d.v_cache;
+    a.k_block_stride = d.k_block_stride;
+    a.v_block_stride = d.v_block_stride;
+    a.num_blocks = d.num_blocks;
+    a.num_kv_heads = d.num_kv_heads;
+    a.head_dim = d.head_dim;
+    uint64_t blocks = 0;
+    hipError_t e = kvp::launch_reshape_and_cache(a, (hipStream_t)stream, &blocks);
+    if (e != hipSuccess)
+        return hip_fail(e, "reshape_and_cache launch");
+    g_cache_launches++;
+    g_last_grid = blocks;
+    return ok();
+}
+
+int32_t kvp_padded_width(int32_t width)
+{
+    if (width <= 0)
+        return 8;
+    return (int32_t)(cdiv(width, 8) * 8);
+}
+
+int kv_prepare_block_tables(const kvp_pool *pool, const int32_t *block_tables, int32_t num_seqs,
+                            int32_t width, const int32_t *seq_lens, int32_t *out)
+{
+    if (!pool || !seq_lens || !out || (num_seqs > 0 && width > 0 && !block_tables))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_prepare_block_tables: null argument");
+    if (num_seqs < 0 || width < 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_prepare_block_tables: negative size");
+    const int64_t nb = pool->d.num_blocks;
+    for (int32_t b = 0; b < num_seqs; ++b) {
+        if (seq_lens[b] < 0)
+            return fail(KVP_ERR_INVALID_ARGUMENT, "kv_prepare_block_tables: seq_lens[%d] < 0", b);
+        const int64_t np = cdiv(seq_lens[b], KVP_BLOCK_SIZE);
+        if (np > width)
+            return fail(KVP_ERR_INVALID_ARGUMENT, "kv_prepare_block_tables: row %d needs %lld pages > width %d", b,
+                        (long long)np, width);
+        for (int64_t c = 0; c < np; ++c) {
+            const int32_t blk = block_tables[(int64_t)b * width + c];
+            if (blk < 0 || blk >= nb)
+                return fail(KVP_ERR_INVALID_ARGUMENT, "kv_prepare_block_tables: block %d at [%d][%lld] outside pool",
+                            blk, b, (long long)c);
+        }
+    }
+    const int32_t wp = kvp_padded_width(width);
+    for (int32_t b = 0; b < num_seqs; ++b) {
+        const int64_t np = cdiv(seq_lens[b], KVP_BLOCK_SIZE);
+        const int32_t *src = block_tables + (int64_t)b * width;
+        const int32_t fill = np > 0 ? src[np - 1] : 0;
+        int32_t *dst = out + (int64_t)b * wp;
+        for (int32_t c = 0; c < wp; ++c)
+            dst[c] = c < np ? src[c] : fill;
+    }
+    return ok();
+}
+
+int kvp_workspace_bytes(const kvp_pool *pool, int32_t num_q_heads, int32_t num_seqs, int32_t max_seq_len,
+                        size_t *bytes)
+{
+    if (!pool || !bytes)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_workspace_bytes: null argument");
+    if (num_q_heads <= 0 || num_seqs < 0 || max_seq_len < 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_workspace_bytes: bad sizes");
+    const int T = kvp::tile_tokens(pool->d.head_dim);
+    const kvp::Workspace w =
+        kvp::workspace_layout(num_seqs, pool->d.num_kv_heads, cdiv(max_seq_len, T), pool->d.head_dim);
+    *bytes = w.total;
+    return ok();
+}
+
+int kvp_workspace_init(void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!workspace || !aligned16(workspace) || workspace_bytes % 16)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_workspace_init: workspace must be 16-byte aligned and sized");
+    uint64_t blocks = 0;
+    hipError_t e = kvp::launch_fill_zero(workspace, workspace_bytes, (hipStream_t)stream, &blocks);
+    if (e != hipSuccess)
+        return hip_fail(e, "kvp_workspace_init launch");
+    g_init_launches++;
+    g_last_grid = blocks;
+    return ok();
+}
+
+int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride, void *out,
+                    int64_t out_token_stride, int32_t num_q_heads, int32_t num_seqs,
+                    const int32_t *block_tables, int32_t block_table_stride, const int32_t *seq_lens,
+                    const int32_t *query_start_loc, int32_t max_query_len, int32_t max_seq_len, float scale,
+                    int causal, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!pool)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: null pool");
+    const kvp_pool_desc &d = pool->d;
+    const int D = d.head_dim;
+    if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
+        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_q_heads %d not a multiple of num_kv_heads %d",
+                    num_q_heads, d.num_kv_heads);
+    const int G = num_q_heads / d.num_kv_heads;
+    if (G > kvp::kSplitCols)
+        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: group size %d > %d", G, kvp::kSplitCols);
+    if (num_seqs < 0 || max_query_len < 0 || max_seq_len < 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: negative size");
+    if (max_query_len > max_seq_len)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: max_query_len %d > max_seq_len %d", max_query_len,
+                    max_seq_len);
+    if (causal != 0 && causal != 1)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: causal must be 0 or 1");
+    if (!std::isfinite(scale))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: scale must be finite");
+    if (num_seqs == 0 || max_query_len == 0)
+        return ok();
+    if (!q || !out || !block_tables || !seq_lens || !query_start_loc)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: null pointer");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: q and out must be 16-byte aligned");
+    const int64_t row = (int64_t)num_q_heads * D;
+    if (q_token_stride < row || out_token_stride < row || q_token_stride % 8 || out_token_stride % 8)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: token strides must be >= %lld and multiples of 8",
+                    (long long)row);
+    if (block_table_stride < cdiv(max_seq_len, KVP_BLOCK_SIZE))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: block_table_stride %d < %lld pages",
+                    block_table_stride, (long long)cdiv(max_seq_len, KVP_BLOCK_SIZE));
+
+    const int T = kvp::tile_tokens(D);
+    kvp::AttnArgs a;
+    a.q = (const uint16_t *)q;
+    a.out = (uint16_t *)out;
+    a.k_cache = (const uint16_t *)d.k_cache;
+    a.v_cache = (const uint16_t *)d.v_cache;
+    a.k_block_stride = d.k_block_stride;
+    a.v_block_stride = d.v_block_stride;
+    a.num_blocks = d.num_blocks;
+    a.q_token_stride = q_token_stride;
+    a.out_token_stride = out_token_stride;
+    a.block_tables = block_tables;
+    a.bt_stride = block_table_stride;
+    a.seq_lens = seq_lens;
+    a.qsl = query_start_loc;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = d.num_kv_heads;
+    a.group = G;
+    a.max_seq_len = max_seq_len;
+    a.max_tiles = (int32_t)cdiv(max_seq_len, T);
+    a.col_groups = 0;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    a.causal = causal;
+    a.ws_acc = a.ws_m = a.ws_l = nullptr;
+    a.ws_ticket = nullptr;
+
+    const bool split = (int64_t)max_query_len * G <= kvp::kSplitCols;
+    if (split) {
+        const kvp::Workspace w = kvp::workspace_layout(num_seqs, d.num_kv_heads, a.max_tiles, D);
+        if (!workspace || !aligned16(workspace))
+            return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: decode needs a 16-byte aligned workspace");
+        if (workspace_bytes < w.total)
+            return fail(KVP_ERR_WORKSPACE_TOO_SMALL, "paged_attention: workspace %zu < %zu bytes", workspace_bytes,
+                        w.total);
+        char *base = (char *)workspace;
+        a.ws_acc = (float *)(base + w.acc_off);
+        a.ws_m = (float *)(base + w.m_off);
+        a.ws_l = (float *)(base + w.l_off);
+        a.ws_ticket = (int32_t *)(base + w.ticket_off);
+        uint64_t blocks = 0;
+        hipError_t e = kvp::launch_split_kv(a, D, (hipStream_t)stream, &blocks);
+        if (e != hipSuccess)
+            return hip_fail(e, "paged_attention split-KV launch");
+        g_split_launches++;
+        g_last_grid = blocks;
+    } else {
+        uint64_t blocks = 0;
+        hipError_t e = kvp::launch_prefill(a, D, max_query_len, (hipStream_t)stream, &blocks);
+        if (e != hipSuccess)
+            return hip_fail(e, "paged_attention prefill launch");
+        g_prefill_launches++;
+        g_last_grid = blocks;
+    }
+    return ok();
+}
+
+int kvp_get_counters(kvp_counters *out)
+{
+    if (!out)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_get_counters: null argument");
+    out->reshape_and_cache_launches = g_cache_launches.load();
+    out->split_kv_launches = g_split_launches.load();
+    out->prefill_launches = g_prefill_launches.load();
+    out->workspace_init_launches = g_init_launches.load();
+    out->last_grid_blocks = g_last_grid.load();
+    return ok();
+}
+
+int kvp_reset_counters(void)
+{
+    g_cache_launches = 0;
+    g_split_launches = 0;
+    g_prefill_launches = 0;
+    g_init_launches = 0;
+    g_last_grid = 0;
+    return ok();
+}
+
+const char *kvp_last_error(void) { return g_err.c_str(); }
+
+const char *kvp_version(void) { return "kvp 0.1 gfx950"; }
+
+}  // extern "C"

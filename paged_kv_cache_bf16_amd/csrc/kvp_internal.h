@@ -1,0 +1,63 @@
+// Internal declarations shared by the host entry points (kvp_api.cpp) and the
+// kernel launchers (cache_kernel.hip, attn_kernel.hip).  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvp.h"
+
+struct kvp_pool {
+    kvp_pool_desc d;
+};
+
+namespace kvp {
+
+// KV tile (keys per softmax tile) for each head size.  Part of the numeric
+// contract: tile boundaries sit at multiples of this many absolute positions.
+constexpr int tile_tokens(int head_dim) { return head_dim == 128 ? 128 : 64; }
+
+// Columns (query position x head-in-group pairs) one split-KV workgroup owns.
+constexpr int kSplitCols = 16;
+
+struct CacheArgs {
+    const uint16_t *k, *v;
+    int64_t num_tokens, k_token_stride, v_token_stride;
+    const int64_t *slot_mapping;
+    uint16_t *k_cache, *v_cache;
+    int64_t k_block_stride, v_block_stride, num_blocks;
+    int32_t num_kv_heads, head_dim;
+};
+
+struct AttnArgs {
+    const uint16_t *q;
+    uint16_t *out;
+    const uint16_t *k_cache, *v_cache;
+    int64_t k_block_stride, v_block_stride, num_blocks;
+    int64_t q_token_stride, out_token_stride;
+    const int32_t *block_tables;
+    int32_t bt_stride;
+    const int32_t *seq_lens, *qsl;
+    int32_t num_seqs, num_q_heads, num_kv_heads, group;
+    int32_t max_seq_len, max_tiles, col_groups;
+    float scale_log2;          // softmax scale * log2(e), rounded once on the host
+    int32_t causal;
+    // split-KV workspace
+    float *ws_acc;             // [B][Hkv][max_tiles][kSplitCols][D]
+    float *ws_m, *ws_l;        // [B][Hkv][max_tiles][kSplitCols]
+    int32_t *ws_ticket;        // [B][Hkv]
+};
+
+struct Workspace {
+    size_t acc_off, m_off, l_off, ticket_off, total;
+};
+
+Workspace workspace_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t max_tiles, int64_t head_dim);
+
+hipError_t launch_reshape_and_cache(const CacheArgs &a, hipStream_t s, uint64_t *blocks);
+hipError_t launch_split_kv(const AttnArgs &a, int head_dim, hipStream_t s, uint64_t *blocks);
+hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s, uint64_t *blocks);
+
+}  // namespace kvp

@@ -1,0 +1,182 @@
+"""CPU tests of the C ABI: the library loads and exports every declared entry
+point; argument validation rejects bad calls before anything is launched;
+page-table preparation (host logic) matches the oracle bit for bit.  No test
+here makes a GPU call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_bf16_amd as kvp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvp.LIB_PATH):
+        from paged_kv_cache_bf16_amd import build
+        build.build()
+    return kvp.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"kv_pool_create", "reshape_and_cache", "paged_attention", "kv_prepare_block_tables",
+            "kvp_workspace_bytes"} <= set(names), names
+    for n in names:
+        assert hasattr(lib, n), "missing export %s" % n
+    assert kvp.kvp_version().startswith("kvp")
+
+
+FAKE_K, FAKE_V = 0x10000000, 0x20000000   # never dereferenced: validation only
+
+
+def make_desc(**kw):
+    d = dict(num_blocks=8, block_size=16, num_kv_heads=2, head_dim=128, reserved=0, k_cache=FAKE_K,
+             v_cache=FAKE_V, k_block_stride=2 * 16 * 128, v_block_stride=2 * 16 * 128)
+    d.update(kw)
+    return kvp.PoolDesc(**d)
+
+
+def create(lib, **kw):
+    h = ctypes.c_void_p()
+    rc = lib.kv_pool_create(ctypes.byref(make_desc(**kw)), ctypes.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), kvp.KVP_ERR_UNSUPPORTED),
+    (dict(block_size=32), kvp.KVP_ERR_UNSUPPORTED),
+    (dict(num_blocks=0), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(k_cache=FAKE_K + 2), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(k_block_stride=100), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(v_cache=FAKE_K + 64), kvp.KVP_ERR_INVALID_ARGUMENT),        # K and V pages overlap
+    (dict(v_cache=None), kvp.KVP_ERR_INVALID_ARGUMENT),
+])
+def test_pool_create_rejects(lib, kw, code):
+    rc, h = create(lib, **kw)
+    assert rc == code
+    assert lib.kvp_last_error().decode()
+
+
+def test_pool_create_interleaved_and_span(lib):
+    page = 2 * 16 * 128
+    rc, h = create(lib, v_cache=FAKE_K + 2 * page, k_block_stride=2 * page, v_block_stride=2 * page,
+                   num_blocks=140000)
+    assert rc == 0, lib.kvp_last_error()
+    span = ctypes.c_int64()
+    assert lib.kv_pool_span_bytes(h, ctypes.byref(span)) == 0
+    assert span.value == 140000 * 2 * page * 2 > 2 ** 31
+    lib.kv_pool_destroy(h)
+
+
+def test_prepare_tables_matches_oracle(lib):
+    rc, h = create(lib, num_blocks=1000)
+    assert rc == 0
+    pool = kvp.KVPool(h, make_desc(num_blocks=1000), None)
+    rng = np.random.default_rng(0)
+    imax = np.iinfo(np.int32).max
+    for trial in range(50):
+        B = int(rng.integers(1, 6))
+        W = int(rng.integers(1, 40))
+        seq = rng.integers(0, 16 * W + 1, size=B).astype(np.int32)
+        bt = rng.integers(0, 1000, size=(B, W)).astype(np.int32)
+        for b in range(B):                        # poison past each row's pages
+            n = -(-int(seq[b]) // 16)
+            bt[b, n:] = rng.choice([-1, imax, 12345678], size=W - n)
+        got = kvp.kv_prepare_block_tables(pool, bt, seq)
+        exp = oracle.prepare_block_tables(bt, seq, 1000)
+        np.testing.assert_array_equal(got, exp)
+        assert got.shape[1] == kvp.kvp_padded_width(W) == -(-W // 8) * 8
+
+
+def test_prepare_tables_rejects_without_writing(lib):
+    rc, h = create(lib, num_blocks=10)
+    pool = kvp.KVPool(h, make_desc(num_blocks=10), None)
+    out = np.full((1, 8), 77, np.int32)
+    bt = np.array([[1, 2, 10]], np.int32)
+    seq = np.array([40], np.int32)
+    rc = lib.kv_prepare_block_tables(h, bt.ctypes.data_as(ctypes.c_void_p), 1, 3,
+                                     seq.ctypes.data_as(ctypes.c_void_p), out.ctypes.data_as(ctypes.c_void_p))
+    assert rc == kvp.KVP_ERR_INVALID_ARGUMENT
+    assert (out == 77).all()
+    with pytest.raises(kvp.KvpError):
+        kvp.kv_prepare_block_tables(pool, np.array([[1, 2]], np.int32), [33])   # needs 3 pages
+
+
+def _attn(lib, h, **kw):
+    a = dict(q=0x30000000, qs=8 * 128, out=0x40000000, os=8 * 128, Hq=8, B=1, bt=0x50000000, bts=8,
+             sl=0x60000000, qsl=0x70000000, mq=1, ms=100, scale=0.1, causal=1, ws=0x80000000, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.paged_attention(h, a["q"], a["qs"], a["out"], a["os"], a["Hq"], a["B"], a["bt"], a["bts"], a["sl"],
+                               a["qsl"], a["mq"], a["ms"], a["scale"], a["causal"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=7), kvp.KVP_ERR_UNSUPPORTED),
+    (dict(Hq=2 * 17), kvp.KVP_ERR_UNSUPPORTED),           # group of 17 > 16
+    (dict(q=0x30000002), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(qs=8 * 128 - 8), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(bts=6), kvp.KVP_ERR_INVALID_ARGUMENT),           # 100 tokens need 7 pages
+    (dict(mq=200), kvp.KVP_ERR_INVALID_ARGUMENT),          # max_query_len > max_seq_len
+    (dict(causal=2), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(wsb=64), kvp.KVP_ERR_WORKSPACE_TOO_SMALL),
+    (dict(sl=None), kvp.KVP_ERR_INVALID_ARGUMENT),
+])
+def test_attention_rejects_before_launch(lib, kw, code):
+    rc, h = create(lib)
+    assert rc == 0
+    kvp.kvp_reset_counters()
+    assert _attn(lib, h, **kw) == code
+    c = kvp.kvp_get_counters()
+    assert c["split_kv_launches"] == 0 and c["prefill_launches"] == 0
+    lib.kv_pool_destroy(h)
+
+
+def test_attention_empty_batch_is_ok_without_launch(lib):
+    rc, h = create(lib)
+    kvp.kvp_reset_counters()
+    assert _attn(lib, h, B=0) == 0
+    assert _attn(lib, h, mq=0) == 0
+    assert kvp.kvp_get_counters()["split_kv_launches"] == 0
+    lib.kv_pool_destroy(h)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(T=-1), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(k=0x30000004), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(ks=100), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(slots=None), kvp.KVP_ERR_INVALID_ARGUMENT),
+])
+def test_reshape_rejects_before_launch(lib, args, code):
+    rc, h = create(lib)
+    a = dict(k=0x30000000, v=0x40000000, T=5, ks=256, vs=256, slots=0x50000000)
+    a.update(args)
+    kvp.kvp_reset_counters()
+    assert lib.reshape_and_cache(h, a["k"], a["v"], a["T"], a["ks"], a["vs"], a["slots"], None) == code
+    assert kvp.kvp_get_counters()["reshape_and_cache_launches"] == 0
+    assert lib.reshape_and_cache(h, a["k"], a["v"], 0, 256, 256, None, None) == 0   # empty is a no-op
+    lib.kv_pool_destroy(h)
+
+
+def test_workspace_bytes_scales_with_tiles(lib):
+    rc, h = create(lib)
+    pool = kvp.KVPool(h, make_desc(), None)
+    a = kvp.kvp_workspace_bytes(pool, 8, 4, 7168)
+    b = kvp.kvp_workspace_bytes(pool, 8, 4, 7168 * 2)
+    assert a >= 4 * 2 * 56 * 16 * 128 * 4 and b > a

@@ -134,11 +134,13 @@ int32_t kvp_padded_width(int32_t width);
 
 /*
  * Bytes of device workspace paged_attention needs for these bounds.  The
- * workspace holds per-tile partial softmax states of the split-KV path and
- * one ticket counter per (sequence, kv head).  Its counters must be zero
- * before the first call (kvp_workspace_init does that); every call leaves
- * them zero again.  One workspace must not be used by two calls that can
- * run at the same time.
+ * workspace starts with 65536 ticket counters (one per sequence x kv head;
+ * decode batches need num_seqs * num_kv_heads <= 65536) followed by the
+ * per-tile partial softmax states of the split-KV path.  The counters must
+ * be zero before the first call (kvp_workspace_init does that); every call
+ * leaves them zero again, so one workspace sized for the largest bounds
+ * serves calls of any smaller batch or length.  One workspace must not be
+ * used by two calls that can run at the same time.
  */
 int kvp_workspace_bytes(const kvp_pool *pool, int32_t num_q_heads, int32_t num_seqs,
                         int32_t max_seq_len, size_t *bytes);

@@ -577,14 +577,18 @@ hipError_t launch_split_kv(const AttnArgs &a, int head_dim, hipStream_t s, uint6
 
 Workspace workspace_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t max_tiles, int64_t head_dim)
 {
+    // The ticket counters sit at a fixed place (the start) whatever the call's
+    // bounds, so calls with different batch sizes or lengths sharing one
+    // workspace always find them zero; the partials after them are fully
+    // rewritten by every call before they are read.
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     Workspace w;
     const size_t slots = (size_t)num_seqs * num_kv_heads * max_tiles * kSplitCols;
-    w.acc_off = 0;
+    w.ticket_off = 0;
+    w.acc_off = (size_t)kMaxTickets * sizeof(int32_t);
     w.m_off = up(w.acc_off + slots * head_dim * sizeof(float));
     w.l_off = up(w.m_off + slots * sizeof(float));
-    w.ticket_off = up(w.l_off + slots * sizeof(float));
-    w.total = up(w.ticket_off + (size_t)num_seqs * num_kv_heads * sizeof(int32_t));
+    w.total = up(w.l_off + slots * sizeof(float));
     return w;
 }
 

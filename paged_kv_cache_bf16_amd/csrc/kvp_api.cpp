@@ -295,6 +295,8 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
     a.ws_ticket = nullptr;
 
     const bool split = (int64_t)max_query_len * G <= kvp::kSplitCols;
+    if (split && (int64_t)num_seqs * d.num_kv_heads > kvp::kMaxTickets)
+        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_seqs * num_kv_heads > %d for decode", kvp::kMaxTickets);
     if (split) {
         const kvp::Workspace w = kvp::workspace_layout(num_seqs, d.num_kv_heads, a.max_tiles, D);
         if (!workspace || !aligned16(workspace))

@@ -21,6 +21,9 @@ constexpr int tile_tokens(int head_dim) { return head_dim == 128 ? 128 : 64; }
 // Columns (query position x head-in-group pairs) one split-KV workgroup owns.
 constexpr int kSplitCols = 16;
 
+// Ticket counters (one per sequence x kv head) at the start of a workspace.
+constexpr int kMaxTickets = 65536;
+
 struct CacheArgs {
     const uint16_t *k, *v;
     int64_t num_tokens, k_token_stride, v_token_stride;

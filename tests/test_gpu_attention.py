@@ -44,9 +44,10 @@ def test_tiny_prefill_and_decode_match_oracle_and_each_other():
 
 def test_tiny_swapped_blocks_change_output():
     """Anti-vacuity: swapping the two in-range logical blocks must change the
-    causal rows (reads really go through the table)."""
+    causal rows (reads really go through the table).  The pool is zero-filled:
+    after the swap some reads land on slots no token wrote."""
     w = wl.tiny()
-    g = GpuCase(w)
+    g = GpuCase(w, fill_bits=0)
     base = g.run()
     bt = w.block_tables.copy()
     bt[0, [0, 1]] = bt[0, [1, 0]]

@@ -133,19 +133,18 @@ int kv_prepare_block_tables(const kvp_pool *pool, const int32_t *block_tables, i
 int32_t kvp_padded_width(int32_t width);
 
 /*
- * Bytes of device workspace paged_attention needs for these bounds.  The
- * workspace starts with 65536 ticket counters (one per sequence x kv head;
- * decode batches need num_seqs * num_kv_heads <= 65536) followed by the
- * per-tile partial softmax states of the split-KV path.  The counters must
- * be zero before the first call (kvp_workspace_init does that); every call
- * leaves them zero again, so one workspace sized for the largest bounds
- * serves calls of any smaller batch or length.  One workspace must not be
- * used by two calls that can run at the same time.
+ * Bytes of device workspace paged_attention needs for these bounds: the
+ * per-tile partial softmax states (m, l, acc) of the split-KV (decode) path.
+ * Every call writes the partials it reads before reading them, so the
+ * workspace needs no initialisation and one workspace sized for the largest
+ * bounds serves calls of any smaller batch or length.  One workspace must
+ * not be used by two calls that can run at the same time.
  */
 int kvp_workspace_bytes(const kvp_pool *pool, int32_t num_q_heads, int32_t num_seqs,
                         int32_t max_seq_len, size_t *bytes);
 
-/* Zero a workspace's counters on `stream` with a fill kernel. */
+/* Zero-fill a workspace on `stream` with a fill kernel (optional; useful to
+ * make a fresh buffer's contents defined). */
 int kvp_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -156,9 +155,10 @@ int kvp_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
  *   q     device, [total_q][num_q_heads][head_dim] BF16, token stride
  *         q_token_stride (elements); total_q = query_start_loc[num_seqs].
  *   out   device, same shape, token stride out_token_stride.
- *   block_tables     device, [num_seqs][block_table_stride] int32, as made
- *                    by kv_prepare_block_tables (block_table_stride >=
- *                    ceil(max_seq_len / 16)).
+ *   block_tables     device, 32-byte aligned, [num_seqs][block_table_stride]
+ *                    int32, as made by kv_prepare_block_tables
+ *                    (block_table_stride a multiple of 8, >= ceil(max_seq_len
+ *                    / 16); whole 128-token tiles of a row are read at once).
  *   seq_lens         device, [num_seqs] int32: KV length of each row.
  *   query_start_loc  device, [num_seqs + 1] int32: row b's queries are
  *                    q[query_start_loc[b] .. query_start_loc[b+1]); they sit

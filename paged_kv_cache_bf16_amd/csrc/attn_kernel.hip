@@ -85,49 +85,73 @@ __device__ __forceinline__ float wave_xor(float v, int mask)
 
 // ---------------------------------------------------------------- staging
 
-// Copies the K and V pages of tile `tile` (kv head kvh) into LDS.  Keys at or
-// beyond seq_len are zero in both; block ids outside the pool read as zero.
+// Block ids of the NKB pages of tile `tile` (wave-uniform), as one vector
+// value (never an indexable array, so lane-dependent choices between two ids
+// stay register selects).  Rows are padded to a multiple of 8 pages (checked
+// on the host), so the whole tile's entries are in the row: one aligned
+// load.  Entries past the row's last page may hold anything and ids outside
+// the pool become 0, so every later load is in bounds; data of keys >=
+// seq_len is discarded by the callers (V zeroed, scores masked).
+template <int NKB>
+using ids_t = int32_t __attribute__((ext_vector_type(NKB)));
+
+template <int NKB>
+__device__ __forceinline__ ids_t<NKB> tile_blocks(const AttnArgs &a, const int32_t *bt_row, int tile)
+{
+    ids_t<NKB> ids = *reinterpret_cast<const ids_t<NKB> *>(bt_row + tile * NKB);
+#pragma unroll
+    for (int i = 0; i < NKB; ++i)
+        ids[i] = (ids[i] < 0 || (int64_t)ids[i] >= a.num_blocks) ? 0 : ids[i];
+    return ids;
+}
+
+// Zero the BF16 elements j of v whose token tok0 + j is >= valid.
+__device__ __forceinline__ u32x4 mask_tokens(u32x4 v, int tok0, int valid)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (tok0 + 2 * j < valid) ? 0x0000FFFFu : 0u;
+        const uint32_t hi = (tok0 + 2 * j + 1 < valid) ? 0xFFFF0000u : 0u;
+        v[j] &= (lo | hi);
+    }
+    return v;
+}
+
+// Copies the K and V pages of tile `tile` (kv head kvh) into LDS.  V of keys
+// at or beyond seq_len is zero; K of those keys is left as read (its scores
+// are masked).  All loads are issued before any is consumed.
 template <int D>
 __device__ __forceinline__ void stage_tile(char *lds, const AttnArgs &a, const int32_t *bt_row,
                                            int seq_len, int kvh, int tile)
 {
     using G = Geo<D>;
+    constexpr int IT = G::NKB * G::UPP / NT;
     char *kl = lds;
     char *vl = lds + G::NKB * G::PAGE;
     const int tid = threadIdx.x;
+    const ids_t<G::NKB> blk = tile_blocks<G::NKB>(a, bt_row, tile);
+    const int64_t hoff = (int64_t)kvh * BS * D;
+    u32x4 kv[IT], vv[IT];
 #pragma unroll
-    for (int it = 0; it < G::NKB * G::UPP / NT; ++it) {
+    for (int it = 0; it < IT; ++it) {
+        const int u = tid + it * NT;
+        const int p = u / G::UPP;           // compile-time per iteration (UPP % NT == 0)
+        const int w = u % G::UPP;
+        kv[it] = *reinterpret_cast<const u32x4 *>(a.k_cache + (int64_t)blk[p] * a.k_block_stride + hoff + (int64_t)w * 8);
+        vv[it] = *reinterpret_cast<const u32x4 *>(a.v_cache + (int64_t)blk[p] * a.v_block_stride + hoff + (int64_t)w * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
         const int u = tid + it * NT;
         const int p = u / G::UPP;
         const int w = u % G::UPP;
-        const int page = tile * G::NKB + p;
-        const int valid = seq_len - page * BS;          // tokens of this page in range
-        u32x4 kval = {0u, 0u, 0u, 0u}, vval = {0u, 0u, 0u, 0u};
-        if (valid > 0) {
-            const int32_t blk = bt_row[page];
-            if (blk >= 0 && (int64_t)blk < a.num_blocks) {
-                const int64_t hoff = (int64_t)kvh * BS * D + (int64_t)w * 8;
-                kval = *reinterpret_cast<const u32x4 *>(a.k_cache + (int64_t)blk * a.k_block_stride + hoff);
-                vval = *reinterpret_cast<const u32x4 *>(a.v_cache + (int64_t)blk * a.v_block_stride + hoff);
-                if (valid < BS) {
-                    // V unit w = (d, half): tokens half*8 .. half*8+7
-                    const int t0 = (w & 1) * 8;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t lo = (t0 + 2 * j < valid) ? 0x0000FFFFu : 0u;
-                        const uint32_t hi = (t0 + 2 * j + 1 < valid) ? 0xFFFF0000u : 0u;
-                        vval[j] &= (lo | hi);
-                    }
-                    // K unit w = (du, tok)
-                    if ((w & 15) >= valid)
-                        kval = u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-        }
+        const int valid = seq_len - (tile * G::NKB + p) * BS;
+        const u32x4 v = valid >= BS ? vv[it] : mask_tokens(vv[it], (w & 1) * 8, valid);
         const int du = w >> 4, tok = w & 15;
-        *reinterpret_cast<u32x4 *>(kl + p * G::PAGE + (du * 16 + ksw(tok, p)) * 16) = kval;
+        *reinterpret_cast<u32x4 *>(kl + p * G::PAGE + (du * 16 + ksw(tok, p)) * 16) = kv[it];
         const int d = w >> 1, half = w & 1;
-        *reinterpret_cast<u32x4 *>(vl + p * G::PAGE + (d * 2 + vsw(half, d)) * 16) = vval;
+        *reinterpret_cast<u32x4 *>(vl + p * G::PAGE + (d * 2 + vsw(half, d)) * 16) = v;
     }
 }
 
@@ -272,8 +296,18 @@ __device__ __forceinline__ float fold_factor(float M, float m, bool &up)
     return m == -INFINITY ? 0.f : f;
 }
 
-// acc' = up ? fma(acc, f, tile) : fma(tile, f, acc).  any_up (wave-uniform)
-// only selects a cheaper instruction sequence with identical results.
+// acc' = up ? fma(acc, f, tile) : fma(tile, f, acc)
+__device__ __forceinline__ float fold1v(float acc, float tile, float f, bool up)
+{
+    const float x = up ? acc : tile;
+    const float y = up ? tile : acc;
+    return __builtin_fmaf(x, f, y);
+}
+
+__device__ __forceinline__ void fold1(float &acc, float tile, float f, bool up) { acc = fold1v(acc, tile, f, up); }
+
+// fold1 on four dims.  any_up (wave-uniform) only selects a cheaper
+// instruction sequence for the common case; the results are identical.
 __device__ __forceinline__ void fold_acc(f32x4 &acc, const f32x4 &tile, float f, bool up, bool any_up)
 {
     if (!any_up) {
@@ -282,11 +316,8 @@ __device__ __forceinline__ void fold_acc(f32x4 &acc, const f32x4 &tile, float f,
             acc[i] = __builtin_fmaf(tile[i], f, acc[i]);
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x = up ? acc[i] : tile[i];
-            const float y = up ? tile[i] : acc[i];
-            acc[i] = __builtin_fmaf(x, f, y);
-        }
+        for (int i = 0; i < 4; ++i)
+            acc[i] = fold1v(acc[i], tile[i], f, up);
     }
 }
 
@@ -296,23 +327,26 @@ __device__ __forceinline__ void fold_stats(float &M, float &L, float m, float l,
     M = up ? m : M;
 }
 
+// bf16 output of one dim: RNE of acc * (1 / L), signed zero made +0
+__device__ __forceinline__ uint16_t finish1(float acc, float inv)
+{
+    const __bf16 r = (__bf16)__fadd_rn(__fmul_rn(acc, inv), 0.f);
+    return __builtin_bit_cast(uint16_t, r);
+}
+
 // bf16 output of 4 consecutive dims
 __device__ __forceinline__ u32x2 finish4(const f32x4 &acc, float inv)
 {
     u32x2 r;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const float a0 = __fadd_rn(__fmul_rn(acc[2 * j], inv), 0.f);
-        const float a1 = __fadd_rn(__fmul_rn(acc[2 * j + 1], inv), 0.f);
-        const __bf16 b0 = (__bf16)a0, b1 = (__bf16)a1;
-        r[j] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-    }
+    for (int j = 0; j < 2; ++j)
+        r[j] = (uint32_t)finish1(acc[2 * j], inv) | ((uint32_t)finish1(acc[2 * j + 1], inv) << 16);
     return r;
 }
 
 // Column bookkeeping: column index -> (query row, head, key limit).
 struct ColInfo {
-    int64_t row;
+    int64_t row, row0;   // the column's query row; the sequence's first query row
     int head;
     int lim;
 };
@@ -323,6 +357,8 @@ __device__ __forceinline__ ColInfo col_info(const AttnArgs &a, int col, int kvh,
     const int pr = col / a.group;
     ci.head = kvh * a.group + col % a.group;
     ci.row = (int64_t)q0 + pr;
+    ci.row0 = q0;
+    ci.head = col < q_len * a.group ? ci.head : kvh * a.group;
     const int pos = seq_len - q_len + pr;
     ci.lim = col < q_len * a.group ? (a.causal ? pos + 1 : seq_len) : 0;
     return ci;
@@ -332,15 +368,13 @@ template <int D>
 __device__ __forceinline__ void load_q(Cols<D> &cf, const AttnArgs &a, const ColInfo &ci)
 {
     const int g = (threadIdx.x & 63) >> 4;
+    // Inactive columns (lim == 0) read the sequence's first query row, which
+    // always exists; every key is masked for them, so their values never
+    // reach a probability.
+    const uint16_t *src = a.q + (ci.lim > 0 ? ci.row : ci.row0) * a.q_token_stride + (int64_t)ci.head * D + 8 * g;
 #pragma unroll
-    for (int ds = 0; ds < Geo<D>::NDS; ++ds) {
-        if (ci.lim > 0) {
-            const uint16_t *src = a.q + ci.row * a.q_token_stride + (int64_t)ci.head * D + 32 * ds + 8 * g;
-            cf.qf[ds] = *reinterpret_cast<const bf16x8 *>(src);
-        } else {
-            cf.qf[ds] = bf16x8{};
-        }
-    }
+    for (int ds = 0; ds < Geo<D>::NDS; ++ds)
+        cf.qf[ds] = *reinterpret_cast<const bf16x8 *>(src + 32 * ds);
     cf.lim = ci.lim;
 }
 
@@ -439,20 +473,33 @@ __global__ __launch_bounds__(NT) void prefill_kernel(AttnArgs a)
 
 // ---------------------------------------------------------------- split-KV (decode)
 
-// Workgroup = (tile, kv head, sequence) for rows whose q_len * G <= 16.
-// All waves stage the tile; wave 0 computes the single column block and
-// stores the tile's partial state.  The last workgroup of a (sequence, kv
-// head) to finish folds the partials in tile order and writes the output.
+// Partial kernel.  Workgroup = (tile, kv head, sequence) for rows whose
+// q_len * G <= 16 (one 16-column block).  The four waves split the tile:
+// wave w owns key blocks [w*KPW, (w+1)*KPW) for S and dim blocks
+// [w*DPW, (w+1)*DPW) for P.V.  K and V fragments are loaded from the pool
+// straight into MFMA operand registers.  The softmax statistics are combined
+// across waves through LDS in exactly the order the single-wave tile step
+// uses (max is exact; the sum tree's first levels are the per-wave sums), so
+// the tile's (m, l, acc) are bitwise those of the prefill tile step.
 template <int D>
-__global__ __launch_bounds__(NT) void split_kv_kernel(AttnArgs a)
+__global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
 {
     using G = Geo<D>;
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    __shared__ int last_flag;
+    constexpr int KPW = G::NKB / NW;   // key blocks per wave
+    constexpr int DPW = G::NDB / NW;   // dim blocks per wave
+    static_assert(KPW == 1 || KPW == 2, "tile shape");
+    __shared__ float smax[NW][16];
+    __shared__ float ssum[NW][64];
+    __shared__ uint32_t spf[NW][2 * KPW][64];
 
     const int tile = blockIdx.x;
     const int kvh = blockIdx.y;
     const int b = blockIdx.z;
+    // The tile's block-table entries are always inside the padded row
+    // (tile < max_tiles), so they are fetched together with the row's
+    // metadata instead of after it.
+    const int32_t *bt_row = a.block_tables + (int64_t)b * a.bt_stride;
+    const ids_t<G::NKB> blk = tile_blocks<G::NKB>(a, bt_row, tile);
     int q0, q_len, seq_len;
     if (!row_ok(a, b, q0, q_len, seq_len))
         return;
@@ -462,60 +509,246 @@ __global__ __launch_bounds__(NT) void split_kv_kernel(AttnArgs a)
     const int n_tiles = (seq_len + G::T - 1) / G::T;
     if (tile >= n_tiles)
         return;
-    const int32_t *bt_row = a.block_tables + (int64_t)b * a.bt_stride;
+    const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, c = lane & 15;
-    const int64_t slot = ((int64_t)b * a.num_kv_heads + kvh) * a.max_tiles;
+    const int64_t hoff = (int64_t)kvh * BS * D;
 
-    stage_tile<D>(lds, a, bt_row, seq_len, kvh, tile);
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        Cols<D> cols;
-        const ColInfo ci = col_info(a, c, kvh, q0, q_len, seq_len);
-        load_q<D>(cols, a, ci);
-        Scores<D> sc;
-        tile_scores<D>(lds, cols, tile, a.scale_log2, sc);
-        float *accp = a.ws_acc + ((slot + tile) * kSplitCols + c) * D + 4 * g;
-        tile_pv<D>(lds, sc, [&](int db, const f32x4 &acc) { *reinterpret_cast<f32x4 *>(accp + 16 * db) = acc; });
-        if (g == 0) {
-            a.ws_m[(slot + tile) * kSplitCols + c] = sc.m;
-            a.ws_l[(slot + tile) * kSplitCols + c] = sc.l;
-        }
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t *ticket = a.ws_ticket + (int64_t)b * a.num_kv_heads + kvh;
-        const int prev = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = prev == n_tiles - 1;
-        if (last)
-            __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = last;
-    }
-    __syncthreads();
-    if (!last_flag)
-        return;
-    __threadfence();
 
-    // Fold: thread -> (column, 4 dims); tiles in ascending order.
-    for (int e = threadIdx.x; e < ncols * (D / 4); e += NT) {
-        const int col = e / (D / 4);
-        const int d4 = (e % (D / 4)) * 4;
-        float M = -INFINITY, L = 0.f;
+    // ---- issue every load of this workgroup up front (no load is conditional)
+    Cols<D> cols;
+    const ColInfo ci = col_info(a, c, kvh, q0, q_len, seq_len);
+    load_q<D>(cols, a, ci);
+    bf16x8 kf[KPW][G::NDS];
+#pragma unroll
+    for (int kl = 0; kl < KPW; ++kl) {
+        const int kb = w * KPW + kl;
+        const int st = kb >> 1, e = kb & 1;
+        const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
+        const int64_t bk = (c >> 3) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
+        const uint16_t *pg = a.k_cache + bk * a.k_block_stride + hoff + tok * 8 + g * 128;
+#pragma unroll
+        for (int ds = 0; ds < G::NDS; ++ds)
+            kf[kl][ds] = *reinterpret_cast<const bf16x8 *>(pg + ds * 512);
+    }
+    u32x4 vraw[DPW][G::NKS];
+#pragma unroll
+    for (int st = 0; st < G::NKS; ++st) {
+        const int64_t bv = (g >> 1) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
+        const uint16_t *pg = a.v_cache + bv * a.v_block_stride + hoff + 8 * (g & 1) + c * 16;
+#pragma unroll
+        for (int dl = 0; dl < DPW; ++dl)
+            vraw[dl][st] = *reinterpret_cast<const u32x4 *>(pg + (16 * (w * DPW + dl)) * 16);
+    }
+    // keep every load above ahead of the first use of any of them
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 vf[DPW][G::NKS];
+#pragma unroll
+    for (int st = 0; st < G::NKS; ++st) {
+        const int valid = seq_len - (tile * G::NKB + 2 * st + (g >> 1)) * BS;
+#pragma unroll
+        for (int dl = 0; dl < DPW; ++dl)
+            vf[dl][st] = __builtin_bit_cast(bf16x8, valid >= BS ? vraw[dl][st] : mask_tokens(vraw[dl][st], 8 * (g & 1), valid));
+    }
+
+    // ---- S for this wave's key blocks; scale, mask, wave max
+    f32x4 s[KPW];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kl = 0; kl < KPW; ++kl) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int t = 0; t < n_tiles; ++t) {
-            const int64_t si = (slot + t) * kSplitCols + col;
-            const float m = a.ws_m[si];
-            const float l = a.ws_l[si];
-            const f32x4 pa = *reinterpret_cast<const f32x4 *>(a.ws_acc + si * D + d4);
-            bool up;
-            const float f = fold_factor(M, m, up);
-            fold_acc(acc, pa, f, up, true);
-            fold_stats(M, L, m, l, f, up);
+#pragma unroll
+        for (int ds = 0; ds < G::NDS; ++ds)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kl][ds], cols.qf[ds], acc, 0, 0, 0);
+        const int kb = w * KPW + kl;
+        const int st = kb >> 1, e = kb & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = tile * G::T + 32 * st + 8 * g + 4 * e + i;
+            const float t = __fmul_rn(acc[i], a.scale_log2);
+            s[kl][i] = key < cols.lim ? t : -INFINITY;
+            mx = fmax2(mx, s[kl][i]);
         }
+    }
+    mx = fmax2(mx, wave_xor(mx, 16));
+    mx = fmax2(mx, wave_xor(mx, 32));
+    if (g == 0)
+        smax[w][c] = mx;
+    __syncthreads();
+    mx = fmax2(fmax2(smax[0][c], smax[1][c]), fmax2(smax[2][c], smax[3][c]));
+    const float mu = mx == -INFINITY ? 0.f : mx;
+
+    // ---- p, this wave's level of the sum tree, P^T values to LDS
+    float part[KPW];
+#pragma unroll
+    for (int kl = 0; kl < KPW; ++kl) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s[kl][i] = __builtin_amdgcn_exp2f(__fsub_rn(s[kl][i], mu));
+        part[kl] = __fadd_rn(__fadd_rn(s[kl][0], s[kl][1]), __fadd_rn(s[kl][2], s[kl][3]));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const __bf16 lo = (__bf16)s[kl][2 * h], hi = (__bf16)s[kl][2 * h + 1];
+            spf[w][2 * kl + h][lane] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                                       ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+    }
+    ssum[w][lane] = KPW == 2 ? __fadd_rn(part[0], part[KPW - 1]) : part[0];
+    __syncthreads();
+
+    // ---- l: remaining levels of the tree, then across lanes
+    float l = __fadd_rn(__fadd_rn(ssum[0][lane], ssum[1][lane]), __fadd_rn(ssum[2][lane], ssum[3][lane]));
+    l = __fadd_rn(l, wave_xor(l, 16));
+    l = __fadd_rn(l, wave_xor(l, 32));
+
+    // ---- P^T operands of every 32-key step, then P.V for this wave's dims
+    bf16x8 pf[G::NKS];
+#pragma unroll
+    for (int st = 0; st < G::NKS; ++st) {
+        u32x4 u;
+        if (KPW == 2) {
+            u = u32x4{spf[st][0][lane], spf[st][1][lane], spf[st][2][lane], spf[st][3][lane]};
+        } else {
+            u = u32x4{spf[2 * st][0][lane], spf[2 * st][1][lane], spf[2 * st + 1][0][lane], spf[2 * st + 1][1][lane]};
+        }
+        pf[st] = __builtin_bit_cast(bf16x8, u);
+    }
+    const int64_t slot = ((int64_t)b * a.num_kv_heads + kvh) * a.max_tiles + tile;
+    float *accp = a.ws_acc + (slot * kSplitCols + c) * D + 4 * g;
+#pragma unroll
+    for (int dl = 0; dl < DPW; ++dl) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < G::NKS; ++st)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dl][st], pf[st], acc, 0, 0, 0);
+        if (c < ncols)
+            *reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)) = acc;
+    }
+    if (w == 0 && g == 0 && c < ncols) {
+        a.ws_m[slot * kSplitCols + c] = mx;
+        a.ws_l[slot * kSplitCols + c] = l;
+    }
+}
+
+// Fold kernel.  Workgroup = (64 consecutive dims of one column, kv head,
+// sequence).  All waves stage the column's per-tile partials into LDS, with
+// every load of a round issued before any is used (the first round is
+// fetched before the row's length is even known: the workspace holds
+// max_tiles slots).  The fold factor of tile t depends only on the running
+// max before t -- the max of the earlier tile maxima, exact in any order --
+// so all factors come from one prefix-max scan; wave 0 then runs the
+// dependent FMA chain in ascending tile order and writes the BF16 output.
+constexpr int kFoldSlice = 64;
+constexpr int kFoldTiles = 192;
+constexpr int kFoldUnits = kFoldTiles * (kFoldSlice / 4) / NT;   // 16-byte loads per thread per round
+
+template <int D>
+__device__ __forceinline__ void fold_stage(const AttnArgs &a, int64_t slot0, int col, int d0, int t0, int nt,
+                                           float (*stage)[kFoldSlice], float *sm, float *sl)
+{
+    const int th = threadIdx.x;
+    f32x4 v[kFoldUnits];
+#pragma unroll
+    for (int r = 0; r < kFoldUnits; ++r) {
+        const int u = th + r * NT;
+        const int tt = min(u / (kFoldSlice / 4), nt - 1);
+        const int q = u % (kFoldSlice / 4);
+        const int64_t si = (slot0 + t0 + tt) * kSplitCols + col;
+        v[r] = *reinterpret_cast<const f32x4 *>(a.ws_acc + si * D + d0 + 4 * q);
+    }
+    float m = 0.f, l = 0.f;
+    if (th < kFoldTiles) {
+        const int64_t si = (slot0 + t0 + min(th, nt - 1)) * kSplitCols + col;
+        m = a.ws_m[si];
+        l = a.ws_l[si];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < kFoldUnits; ++r) {
+        const int u = th + r * NT;
+        const int tt = u / (kFoldSlice / 4);
+        if (tt < nt)
+            *reinterpret_cast<f32x4 *>(&stage[tt][4 * (u % (kFoldSlice / 4))]) = v[r];
+    }
+    if (th < nt) {
+        sm[th] = m;
+        sl[th] = l;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
+{
+    using G = Geo<D>;
+    constexpr int NSL = D / kFoldSlice;
+    __shared__ float stage[kFoldTiles][kFoldSlice];
+    __shared__ float sm[kFoldTiles], sl[kFoldTiles], sf[kFoldTiles];
+    __shared__ int sup[kFoldTiles];
+    __shared__ float wmax[NW];
+
+    const int slice = blockIdx.x % NSL;
+    const int col = blockIdx.x / NSL;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int64_t slot0 = ((int64_t)b * a.num_kv_heads + kvh) * a.max_tiles;
+    const int d0 = slice * kFoldSlice;
+    const int th = threadIdx.x, lane = th & 63, w = th >> 6;
+
+    // first round staged speculatively for min(max_tiles, kFoldTiles) tiles
+    const int nt0 = min(kFoldTiles, a.max_tiles);
+    fold_stage<D>(a, slot0, col, d0, 0, nt0, stage, sm, sl);
+
+    int q0, q_len, seq_len;
+    if (!row_ok(a, b, q0, q_len, seq_len))
+        return;
+    const int ncols = q_len * a.group;
+    if (ncols > kSplitCols || col >= ncols)
+        return;
+    const int n_tiles = (seq_len + G::T - 1) / G::T;
+
+    float M = -INFINITY, L = 0.f, acc = 0.f;
+    for (int t0 = 0; t0 < n_tiles; t0 += kFoldTiles) {
+        const int nt = min(kFoldTiles, n_tiles - t0);
+        if (t0 > 0) {
+            __syncthreads();
+            fold_stage<D>(a, slot0, col, d0, t0, nt, stage, sm, sl);
+        }
+        __syncthreads();
+        // running max before each tile: inclusive wave scans, then wave totals
+        float v = th < nt ? sm[th] : -INFINITY;
+#pragma unroll
+        for (int off = 1; off < 64; off *= 2) {
+            const float o = __shfl_up(v, off, 64);
+            v = lane >= off ? fmax2(v, o) : v;
+        }
+        if (lane == 63)
+            wmax[w] = v;
+        __syncthreads();
+        float pre = M;
+        for (int k = 0; k < w; ++k)
+            pre = fmax2(pre, wmax[k]);
+        const float incl = fmax2(pre, v);
+        float excl = __shfl_up(incl, 1, 64);
+        excl = lane == 0 ? pre : excl;
+        if (th < nt) {
+            bool up;
+            sf[th] = fold_factor(excl, sm[th], up);
+            sup[th] = up;
+        }
+        __syncthreads();
+        if (th < kFoldSlice) {
+#pragma unroll 8
+            for (int tt = 0; tt < nt; ++tt)
+                acc = fold1v(acc, stage[tt][th], sf[tt], sup[tt] != 0);
+        }
+        // every thread carries (M, L): the next round's scan starts from M
+#pragma unroll 8
+        for (int tt = 0; tt < nt; ++tt)
+            fold_stats(M, L, sm[tt], sl[tt], sf[tt], sup[tt] != 0);
+    }
+    if (th < kFoldSlice) {
         const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
-        const float inv = 1.0f / L;
-        *reinterpret_cast<u32x2 *>(a.out + ci.row * a.out_token_stride + (int64_t)ci.head * D + d4) = finish4(acc, inv);
+        a.out[ci.row * a.out_token_stride + (int64_t)ci.head * D + d0 + th] = finish1(acc, 1.0f / L);
     }
 }
 
@@ -554,13 +787,12 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
 template <int D>
 static hipError_t split_launch(const AttnArgs &a, hipStream_t s, uint64_t *blocks)
 {
-    const dim3 grid((unsigned)a.max_tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     if (a.max_tiles <= 0 || a.num_seqs <= 0)
         return hipSuccess;
-    static const hipError_t attr = hipFuncSetAttribute((const void *)split_kv_kernel<D>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, Geo<D>::LDS);
-    (void)attr;
-    hipLaunchKernelGGL((split_kv_kernel<D>), grid, dim3(NT), Geo<D>::LDS, s, a);
+    const dim3 grid((unsigned)a.max_tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+    hipLaunchKernelGGL((split_partial_kernel<D>), grid, dim3(NT), 0, s, a);
+    const dim3 fgrid((unsigned)(kSplitCols * (D / kFoldSlice)), (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+    hipLaunchKernelGGL((split_fold_kernel<D>), fgrid, dim3(NT), 0, s, a);
     *blocks = (uint64_t)a.max_tiles * a.num_kv_heads * a.num_seqs;
     return hipGetLastError();
 }
@@ -577,15 +809,13 @@ hipError_t launch_split_kv(const AttnArgs &a, int head_dim, hipStream_t s, uint6
 
 Workspace workspace_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t max_tiles, int64_t head_dim)
 {
-    // The ticket counters sit at a fixed place (the start) whatever the call's
-    // bounds, so calls with different batch sizes or lengths sharing one
-    // workspace always find them zero; the partials after them are fully
-    // rewritten by every call before they are read.
+    // Per-tile partials of the split-KV path.  Every call rewrites the slots
+    // it reads before reading them, so the workspace needs no initialisation
+    // and one workspace sized for the largest bounds serves smaller calls.
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     Workspace w;
     const size_t slots = (size_t)num_seqs * num_kv_heads * max_tiles * kSplitCols;
-    w.ticket_off = 0;
-    w.acc_off = (size_t)kMaxTickets * sizeof(int32_t);
+    w.acc_off = 0;
     w.m_off = up(w.acc_off + slots * head_dim * sizeof(float));
     w.l_off = up(w.m_off + slots * sizeof(float));
     w.total = up(w.l_off + slots * sizeof(float));

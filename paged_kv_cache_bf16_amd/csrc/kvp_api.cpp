@@ -263,9 +263,12 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
     if (q_token_stride < row || out_token_stride < row || q_token_stride % 8 || out_token_stride % 8)
         return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: token strides must be >= %lld and multiples of 8",
                     (long long)row);
-    if (block_table_stride < cdiv(max_seq_len, KVP_BLOCK_SIZE))
-        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: block_table_stride %d < %lld pages",
+    if (block_table_stride < cdiv(max_seq_len, KVP_BLOCK_SIZE) || block_table_stride % 8)
+        return fail(KVP_ERR_INVALID_ARGUMENT,
+                    "paged_attention: block_table_stride %d must be a multiple of 8 and >= %lld pages",
                     block_table_stride, (long long)cdiv(max_seq_len, KVP_BLOCK_SIZE));
+    if (((uintptr_t)block_tables & 31u) != 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: block_tables must be 32-byte aligned");
 
     const int T = kvp::tile_tokens(D);
     kvp::AttnArgs a;
@@ -292,11 +295,10 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
     a.scale_log2 = scale * 1.44269504088896340736f;
     a.causal = causal;
     a.ws_acc = a.ws_m = a.ws_l = nullptr;
-    a.ws_ticket = nullptr;
 
     const bool split = (int64_t)max_query_len * G <= kvp::kSplitCols;
-    if (split && (int64_t)num_seqs * d.num_kv_heads > kvp::kMaxTickets)
-        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_seqs * num_kv_heads > %d for decode", kvp::kMaxTickets);
+    if (num_seqs > 65535 || d.num_kv_heads > 65535)
+        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_seqs and num_kv_heads must be <= 65535");
     if (split) {
         const kvp::Workspace w = kvp::workspace_layout(num_seqs, d.num_kv_heads, a.max_tiles, D);
         if (!workspace || !aligned16(workspace))
@@ -308,7 +310,6 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
         a.ws_acc = (float *)(base + w.acc_off);
         a.ws_m = (float *)(base + w.m_off);
         a.ws_l = (float *)(base + w.l_off);
-        a.ws_ticket = (int32_t *)(base + w.ticket_off);
         uint64_t blocks = 0;
         hipError_t e = kvp::launch_split_kv(a, D, (hipStream_t)stream, &blocks);
         if (e != hipSuccess)

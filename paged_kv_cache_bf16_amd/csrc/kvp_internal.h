@@ -21,9 +21,6 @@ constexpr int tile_tokens(int head_dim) { return head_dim == 128 ? 128 : 64; }
 // Columns (query position x head-in-group pairs) one split-KV workgroup owns.
 constexpr int kSplitCols = 16;
 
-// Ticket counters (one per sequence x kv head) at the start of a workspace.
-constexpr int kMaxTickets = 65536;
-
 struct CacheArgs {
     const uint16_t *k, *v;
     int64_t num_tokens, k_token_stride, v_token_stride;
@@ -49,16 +46,16 @@ struct AttnArgs {
     // split-KV workspace
     float *ws_acc;             // [B][Hkv][max_tiles][kSplitCols][D]
     float *ws_m, *ws_l;        // [B][Hkv][max_tiles][kSplitCols]
-    int32_t *ws_ticket;        // [B][Hkv]
 };
 
 struct Workspace {
-    size_t acc_off, m_off, l_off, ticket_off, total;
+    size_t acc_off, m_off, l_off, total;
 };
 
 Workspace workspace_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t max_tiles, int64_t head_dim);
 
 hipError_t launch_reshape_and_cache(const CacheArgs &a, hipStream_t s, uint64_t *blocks);
+// Split-KV path: per-tile partial kernel, then the fold kernel.
 hipError_t launch_split_kv(const AttnArgs &a, int head_dim, hipStream_t s, uint64_t *blocks);
 hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s, uint64_t *blocks);

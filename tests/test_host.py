@@ -131,6 +131,8 @@ def _attn(lib, h, **kw):
     (dict(q=0x30000002), kvp.KVP_ERR_INVALID_ARGUMENT),
     (dict(qs=8 * 128 - 8), kvp.KVP_ERR_INVALID_ARGUMENT),
     (dict(bts=6), kvp.KVP_ERR_INVALID_ARGUMENT),           # 100 tokens need 7 pages
+    (dict(bts=12, ms=10), kvp.KVP_ERR_INVALID_ARGUMENT),   # stride not a multiple of 8
+    (dict(bt=0x50000010), kvp.KVP_ERR_INVALID_ARGUMENT),   # table not 32-byte aligned
     (dict(mq=200), kvp.KVP_ERR_INVALID_ARGUMENT),          # max_query_len > max_seq_len
     (dict(causal=2), kvp.KVP_ERR_INVALID_ARGUMENT),
     (dict(scale=float("nan")), kvp.KVP_ERR_INVALID_ARGUMENT),

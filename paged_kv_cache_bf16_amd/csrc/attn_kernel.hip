@@ -398,12 +398,183 @@ __device__ __forceinline__ bool row_ok(const AttnArgs &a, int b, int &q0, int &q
     return q_len > 0 && q_len <= seq_len && seq_len <= a.max_seq_len && q0 >= 0;
 }
 
+// ---------------------------------------------------------------- joint tile step (prefill)
+
+// One tile for CB column blocks of a wave, folded into their states.  Per
+// column this is exactly tile_scores + tile_pv + the fold (same MFMA chains,
+// same softmax operations and tree, same fold); only independent chains of
+// different column blocks are interleaved, each K / V fragment read from LDS
+// once for all CB blocks, and fragment reads are software-pipelined one
+// step ahead (scheduling barriers keep the compiler from hoisting every read
+// to the top, which would multiply the register footprint).  need_mask is
+// false when every column of the wave sees every key of the tile; the
+// multiply-only path then gives the same values as the masked one.
+template <int D, int CB>
+__device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&cols)[CB], int tile, float scale_log2,
+                                             State<D> (&st)[CB], bool need_mask)
+{
+    using G = Geo<D>;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    const char *kl = lds;
+    const char *vl = lds + G::NKB * G::PAGE;
+
+    auto kaddr = [&](int kb) -> const char * {
+        const int stp = kb >> 1, e = kb & 1;
+        const int page = 2 * stp + (c >> 3);
+        const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
+        return kl + page * G::PAGE + ksw(tok, page) * 16 + g * 256;
+    };
+    // ---- S^T = K . Q^T for every column block
+    f32x4 s[CB][G::NKB];
+    bf16x8 kf[G::NDS], kn[G::NDS];
+    {
+        const char *p0 = kaddr(0);
+#pragma unroll
+        for (int ds = 0; ds < G::NDS; ++ds)
+            kf[ds] = *reinterpret_cast<const bf16x8 *>(p0 + ds * 1024);
+    }
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb) {
+        if (kb + 1 < G::NKB) {
+            const char *pn = kaddr(kb + 1);
+#pragma unroll
+            for (int ds = 0; ds < G::NDS; ++ds)
+                kn[ds] = *reinterpret_cast<const bf16x8 *>(pn + ds * 1024);
+        }
+        f32x4 acc[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < G::NDS; ++ds)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ds], cols[cb].qf[ds], acc[cb], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            s[cb][kb] = acc[cb];
+#pragma unroll
+        for (int ds = 0; ds < G::NDS; ++ds)
+            kf[ds] = kn[ds];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- softmax statistics and P^T per column block
+    const int key0 = tile * G::T;
+    float mx[CB], lsum[CB];
+    bf16x8 pf[CB][G::NKS];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        float m = -INFINITY;
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < G::NKB; ++kb) {
+                const int stp = kb >> 1, e = kb & 1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = key0 + 32 * stp + 8 * g + 4 * e + i;
+                    const float t = __fmul_rn(s[cb][kb][i], scale_log2);
+                    s[cb][kb][i] = key < cols[cb].lim ? t : -INFINITY;
+                    m = fmax2(m, s[cb][kb][i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s[cb][kb][i] = __fmul_rn(s[cb][kb][i], scale_log2);
+                    m = fmax2(m, s[cb][kb][i]);
+                }
+        }
+        m = fmax2(m, wave_xor(m, 16));
+        m = fmax2(m, wave_xor(m, 32));
+        const float mu = m == -INFINITY ? 0.f : m;
+        float part[G::NKB];
+#pragma unroll
+        for (int kb = 0; kb < G::NKB; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s[cb][kb][i] = __builtin_amdgcn_exp2f(__fsub_rn(s[cb][kb][i], mu));
+            part[kb] = __fadd_rn(__fadd_rn(s[cb][kb][0], s[cb][kb][1]), __fadd_rn(s[cb][kb][2], s[cb][kb][3]));
+        }
+#pragma unroll
+        for (int w = 1; w < G::NKB; w *= 2)
+#pragma unroll
+            for (int kb = 0; kb < G::NKB; kb += 2 * w)
+                part[kb] = __fadd_rn(part[kb], part[kb + w]);
+        float l = part[0];
+        l = __fadd_rn(l, wave_xor(l, 16));
+        l = __fadd_rn(l, wave_xor(l, 32));
+        mx[cb] = m;
+        lsum[cb] = l;
+#pragma unroll
+        for (int stp = 0; stp < G::NKS; ++stp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pf[cb][stp][i] = (__bf16)s[cb][2 * stp][i];
+                pf[cb][stp][4 + i] = (__bf16)s[cb][2 * stp + 1][i];
+            }
+    }
+
+    // ---- fold factors
+    float f[CB];
+    bool up[CB], any_up[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        f[cb] = fold_factor(st[cb].M, mx[cb], up[cb]);
+        any_up[cb] = __ballot(up[cb]) != 0;
+    }
+
+    // ---- O^T = V^T . P^T per 16-dim block, folded straight into the states
+    auto vaddr = [&](int db) -> const char * {
+        const int d = 16 * db + c;
+        return vl + (g >> 1) * G::PAGE + (d * 2 + vsw(g & 1, d)) * 16;
+    };
+    bf16x8 vf[G::NKS], vn[G::NKS];
+    {
+        const char *p0 = vaddr(0);
+#pragma unroll
+        for (int stp = 0; stp < G::NKS; ++stp)
+            vf[stp] = *reinterpret_cast<const bf16x8 *>(p0 + 2 * stp * G::PAGE);
+    }
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+        if (db + 1 < G::NDB) {
+            const char *pn = vaddr(db + 1);
+#pragma unroll
+            for (int stp = 0; stp < G::NKS; ++stp)
+                vn[stp] = *reinterpret_cast<const bf16x8 *>(pn + 2 * stp * G::PAGE);
+        }
+        f32x4 acc[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int stp = 0; stp < G::NKS; ++stp)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[stp], pf[cb][stp], acc[cb], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            fold_acc(st[cb].acc[db], acc[cb], f[cb], up[cb], any_up[cb]);
+#pragma unroll
+        for (int stp = 0; stp < G::NKS; ++stp)
+            vf[stp] = vn[stp];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        fold_stats(st[cb].M, st[cb].L, mx[cb], lsum[cb], f[cb], up[cb]);
+}
+
 // ---------------------------------------------------------------- streaming prefill
 
 // Workgroup = (column group, kv head, sequence); 4 waves x CB column blocks.
 // Walks the tiles in ascending order, folding each into registers.
 template <int D, int CB>
-__global__ __launch_bounds__(NT) void prefill_kernel(AttnArgs a)
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 512 ? 1 : 2, 2))) void prefill_kernel(AttnArgs a)
 {
     using G = Geo<D>;
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -447,23 +618,22 @@ __global__ __launch_bounds__(NT) void prefill_kernel(AttnArgs a)
         active |= (cg * NCOL + (wave * CB + cb) * 16) < ncols;
     }
 
+    // smallest key limit of the wave's columns: tiles ending at or below it
+    // need no mask
+    int min_lim = 0x7fffffff;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        min_lim = min(min_lim, cols[cb].lim);
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2)
+        min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
+
     for (int tile = 0; tile <= last_tile; ++tile) {
         __syncthreads();
         stage_tile<D>(lds, a, bt_row, seq_len, kvh, tile);
         __syncthreads();
-        if (active) {
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-                Scores<D> sc;
-                tile_scores<D>(lds, cols[cb], tile, a.scale_log2, sc);
-                bool up;
-                const float f = fold_factor(st[cb].M, sc.m, up);
-                const bool any_up = __ballot(up) != 0;
-                State<D> &S = st[cb];
-                tile_pv<D>(lds, sc, [&](int db, const f32x4 &acc) { fold_acc(S.acc[db], acc, f, up, any_up); });
-                fold_stats(S.M, S.L, sc.m, sc.l, f, up);
-            }
-        }
+        if (active)
+            prefill_tile<D, CB>(lds, cols, tile, a.scale_log2, st, (tile + 1) * G::T > min_lim);
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)

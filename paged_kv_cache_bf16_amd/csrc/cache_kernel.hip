@@ -22,11 +22,11 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void cache_k_kernel(CacheArgs a)
+__device__ __forceinline__ void cache_k(const CacheArgs &a, int64_t blk_id)
 {
     const int units_per_head = a.head_dim / 8;
     const int64_t units = a.num_tokens * a.num_kv_heads * units_per_head;
-    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t u = blk_id * blockDim.x + threadIdx.x;
     if (u >= units)
         return;
     const int du = (int)(u % units_per_head);
@@ -44,12 +44,12 @@ __global__ __launch_bounds__(256) void cache_k_kernel(CacheArgs a)
     *reinterpret_cast<u32x4 *>(dst) = val;
 }
 
-// grid.x covers (head, dim-group) x token-chunks of 64; lane = token in chunk.
-__global__ __launch_bounds__(256) void cache_v_kernel(CacheArgs a)
+// Waves cover (head, dim-group) x token-chunks of 64; lane = token in chunk.
+__device__ __forceinline__ void cache_v(const CacheArgs &a, int64_t blk_id)
 {
     const int units_per_head = a.head_dim / 8;
     const int64_t chunks = (a.num_tokens + 63) / 64;
-    const int64_t w = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64;   // wave id
+    const int64_t w = (blk_id * blockDim.x + threadIdx.x) / 64;   // wave id
     const int lane = threadIdx.x % 64;
     const int64_t per_token_units = (int64_t)a.num_kv_heads * units_per_head;
     if (w >= chunks * per_token_units)
@@ -75,6 +75,16 @@ __global__ __launch_bounds__(256) void cache_v_kernel(CacheArgs a)
     }
 }
 
+// One launch for both halves: workgroups [0, k_blocks) copy K, the rest V.
+__global__ __launch_bounds__(256) void cache_kernel(CacheArgs a, int64_t k_blocks)
+{
+    const int64_t bid = blockIdx.x;
+    if (bid < k_blocks)
+        cache_k(a, bid);
+    else
+        cache_v(a, bid - k_blocks);
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(u32x4 *p, int64_t n16)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -90,12 +100,10 @@ hipError_t launch_reshape_and_cache(const CacheArgs &a, hipStream_t s, uint64_t 
     const int64_t gk = (units + 255) / 256;
     const int64_t waves = ((a.num_tokens + 63) / 64) * a.num_kv_heads * (a.head_dim / 8);
     const int64_t gv = (waves + 3) / 4;
-    if (gk > 0x7fffffff || gv > 0x7fffffff)
+    if (gk + gv > 0x7fffffff)
         return hipErrorInvalidValue;
-    if (gk > 0)
-        hipLaunchKernelGGL(cache_k_kernel, dim3((unsigned)gk), dim3(256), 0, s, a);
-    if (gv > 0)
-        hipLaunchKernelGGL(cache_v_kernel, dim3((unsigned)gv), dim3(256), 0, s, a);
+    if (gk + gv > 0)
+        hipLaunchKernelGGL(cache_kernel, dim3((unsigned)(gk + gv)), dim3(256), 0, s, a, gk);
     *blocks = (uint64_t)(gk + gv);
     return hipGetLastError();
 }

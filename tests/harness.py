@@ -32,7 +32,7 @@ class GpuCase:
     """A workload resident on the GPU: pool filled through reshape_and_cache,
     prepared tables and metadata, and a workspace."""
 
-    def __init__(self, w: wl.Workload, fill_bits=POISON):
+    def __init__(self, w: wl.Workload, fill_bits=POISON, ws_max_seq_len=None):
         self.w = w
         self.pool = kvp.alloc_pool(w.num_blocks, w.num_kv_heads, w.head_dim, interleaved=w.interleaved,
                                    fill_bits=fill_bits)
@@ -41,7 +41,8 @@ class GpuCase:
         self.slots = torch.from_numpy(w.slot_mapping).cuda()
         kvp.reshape_and_cache(self.pool, self.k, self.v, self.slots)
         self.set_queries(w.q, w.query_lens)
-        self.ws = kvp.alloc_workspace(self.pool, w.num_q_heads, w.batch, int(w.seq_lens.max(initial=1)))
+        self.ws = kvp.alloc_workspace(self.pool, w.num_q_heads, w.batch,
+                                      int(ws_max_seq_len or w.seq_lens.max(initial=1)))
 
     def set_queries(self, q_bits, query_lens, block_tables=None, seq_lens=None):
         w = self.w
@@ -59,11 +60,14 @@ class GpuCase:
         self.q = dev_bits(q_bits)
         self.out = torch.zeros_like(self.q)
 
-    def run(self, causal=None):
+    def run(self, causal=None, max_seq_len=None):
+        """Run paged_attention; max_seq_len overrides the host bound (it must
+        cover every row; a larger bound can select a different kernel path)."""
         w = self.w
         self.out.fill_(-1)                         # 0xFFFF: NaN bits, so unwritten rows show
+        ms = int(self.seq_lens_h.max(initial=0)) if max_seq_len is None else int(max_seq_len)
         kvp.paged_attention(self.pool, self.q, self.out, w.num_q_heads, self.bt, self.seq_lens, self.qsl,
-                            int(self.qlens_h.max(initial=0)), int(self.seq_lens_h.max(initial=0)), w.scale,
+                            int(self.qlens_h.max(initial=0)), ms, w.scale,
                             w.causal if causal is None else causal, workspace=self.ws)
         torch.cuda.synchronize()
         return host_bits(self.out)

@@ -177,6 +177,19 @@ def test_page_permutation_and_batch_shape_are_bitwise_neutral():
     bitwise(g.run(), base[2:3], "row 2 alone")
 
 
+def test_decode_with_larger_host_bound_is_bitwise_equal():
+    """A looser max_seq_len bound (wider grid, more empty tiles) changes who
+    computes, never what: the same rows give the same bits."""
+    lens = [4000, 129, 1, 7000]
+    w = wl.random_case(17, lens, [1] * 4, 8, 2, 128)
+    g = GpuCase(w, ws_max_seq_len=8400)
+    base = g.run()
+    wide_bt = np.pad(w.block_tables, ((0, 0), (0, 100)))
+    g.set_queries(w.q, w.query_lens, block_tables=wide_bt)
+    bitwise(base, g.run(max_seq_len=8400), "looser max_seq_len")
+    compare(base, oracle_attention(w, oracle_pool(w)), "decode")
+
+
 def test_repeated_calls_are_deterministic_and_workspace_self_cleans():
     w = wl.random_case(12, [3000, 40], [1, 1], 8, 2, 128)
     g = GpuCase(w)

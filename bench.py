@@ -201,6 +201,32 @@ class PrefillBench:
         self.attention()
 
 
+COUNTERS = os.path.join(ROOT, "profiles", "bench_default_hbm_counters.md")
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_bf16_amd", "csrc", "attn_kernel.hip")
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch (read + write) of `kernel` from the committed rocprofv3
+    counter summary, or None when that summary was taken on other kernel source."""
+    import hashlib
+    try:
+        text = open(COUNTERS).read()
+    except OSError:
+        return None
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if ("kernel_source_sha256: " + sha) not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic " + kernel + " "):
+            f = dict(x.split("=") for x in line.split()[2:])
+            return int(f["read_bytes"]) + int(f["write_bytes"])
+    return None
+
+
+def _sum_or_none(*xs):
+    return None if any(x is None for x in xs) else sum(xs)
+
+
 def _omp_threads():
     try:
         aff = len(os.sched_getaffinity(0))
@@ -219,6 +245,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run 3 device copies of this many MiB (a known-size kernel for HBM counter scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -231,6 +259,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration: 3 copies of %d MiB (read %d B + write %d B each)" % (args.calibrate_copy_mib, 4 * n, 4 * n))
+        del src, dst
 
     log("setting up decode workload (%d page sets)" % args.sets)
     dec = DecodeBench(sets=args.sets)
@@ -284,7 +322,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec.algo_bytes / (attn_us * 1e-6) / 1e9, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec.algo_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "split_kv_kernel<128>", "us_per_call": round(attn_us, 3),
+                     "traffic": _sum_or_none(recorded_traffic("split_partial_kernel<128>"),
+                                             recorded_traffic("split_fold_kernel<128>")),
+                     "kernel": "split_partial_kernel<128> + split_fold_kernel<128> (one paged_attention call)",
+                     "us_per_call": round(attn_us, 3),
                      "algo_bytes_per_call": dec.algo_bytes},
         "decode_warm_cache": {"us_per_call": round(warm_us, 3),
                               "GBps": round(dec.algo_bytes / (warm_us * 1e-6) / 1e9, 1)},
@@ -307,7 +348,8 @@ def main():
                              "us_per_call": round(p_us, 2), "us_per_step_with_cache_write": round(step_us, 2),
                              "TFLOPs": round(tf, 2), "peak_TFLOPs": BF16_PEAK_TFLOPS,
                              "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops_per_call": pre.flops,
-                             "kernel": "prefill_kernel<128,2>"}
+                             "kernel": "prefill_kernel<128, 2>",
+                             "hbm_traffic_bytes": recorded_traffic("prefill_kernel<128,2>")}
         log("prefill: %.2f us/call, %.1f TFLOP/s" % (p_us, tf))
         del pre
 

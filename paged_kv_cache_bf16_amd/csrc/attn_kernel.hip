@@ -955,24 +955,26 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
 }
 
 template <int D>
-static hipError_t split_launch(const AttnArgs &a, hipStream_t s, uint64_t *blocks)
+static hipError_t split_launch(const AttnArgs &a, int max_query_len, hipStream_t s, uint64_t *blocks)
 {
     if (a.max_tiles <= 0 || a.num_seqs <= 0)
         return hipSuccess;
     const dim3 grid((unsigned)a.max_tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     hipLaunchKernelGGL((split_partial_kernel<D>), grid, dim3(NT), 0, s, a);
-    const dim3 fgrid((unsigned)(kSplitCols * (D / kFoldSlice)), (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+    // one fold workgroup per (column that can exist, 64-dim slice)
+    const int max_cols = min(kSplitCols, max_query_len * a.group);
+    const dim3 fgrid((unsigned)(max_cols * (D / kFoldSlice)), (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     hipLaunchKernelGGL((split_fold_kernel<D>), fgrid, dim3(NT), 0, s, a);
     *blocks = (uint64_t)a.max_tiles * a.num_kv_heads * a.num_seqs;
     return hipGetLastError();
 }
 
-hipError_t launch_split_kv(const AttnArgs &a, int head_dim, hipStream_t s, uint64_t *blocks)
+hipError_t launch_split_kv(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks)
 {
     switch (head_dim) {
-    case 128: return split_launch<128>(a, s, blocks);
-    case 256: return split_launch<256>(a, s, blocks);
-    case 512: return split_launch<512>(a, s, blocks);
+    case 128: return split_launch<128>(a, max_query_len, s, blocks);
+    case 256: return split_launch<256>(a, max_query_len, s, blocks);
+    case 512: return split_launch<512>(a, max_query_len, s, blocks);
     default: return hipErrorInvalidValue;
     }
 }

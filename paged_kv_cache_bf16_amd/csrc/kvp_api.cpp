@@ -311,7 +311,7 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
         a.ws_m = (float *)(base + w.m_off);
         a.ws_l = (float *)(base + w.l_off);
         uint64_t blocks = 0;
-        hipError_t e = kvp::launch_split_kv(a, D, (hipStream_t)stream, &blocks);
+        hipError_t e = kvp::launch_split_kv(a, D, max_query_len, (hipStream_t)stream, &blocks);
         if (e != hipSuccess)
             return hip_fail(e, "paged_attention split-KV launch");
         g_split_launches++;

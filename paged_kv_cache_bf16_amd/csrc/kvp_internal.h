@@ -56,7 +56,7 @@ Workspace workspace_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t max_t
 
 hipError_t launch_reshape_and_cache(const CacheArgs &a, hipStream_t s, uint64_t *blocks);
 // Split-KV path: per-tile partial kernel, then the fold kernel.
-hipError_t launch_split_kv(const AttnArgs &a, int head_dim, hipStream_t s, uint64_t *blocks);
+hipError_t launch_split_kv(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks);
 hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s, uint64_t *blocks);
 

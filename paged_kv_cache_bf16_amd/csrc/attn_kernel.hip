@@ -78,9 +78,31 @@ __device__ __forceinline__ int vsw(int half, int d)
 
 __device__ __forceinline__ float fmax2(float a, float b) { return a > b ? a : b; }
 
-__device__ __forceinline__ float wave_xor(float v, int mask)
+// Cross-lane steps of the softmax reductions, lane l combined with lane
+// l ^ 16, then with lane l ^ 32, using the gfx950 row / half swaps (VALU, no
+// LDS round trip).  With both operands the same register, the two halves of
+// the swap result hold x[l] and x[l ^ 16] (resp. x[l ^ 32]) in some order on
+// every lane, and both combining operations are commutative, so every lane
+// gets the same bits as x[l] op x[l ^ k].
+__device__ __forceinline__ float sum_xor16(float v)
 {
-    return __shfl_xor(v, mask, 64);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __fadd_rn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __fadd_rn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // ---------------------------------------------------------------- staging
@@ -141,17 +163,25 @@ __device__ __forceinline__ void stage_tile(char *lds, const AttnArgs &a, const i
         vv[it] = *reinterpret_cast<const u32x4 *>(a.v_cache + (int64_t)blk[p] * a.v_block_stride + hoff + (int64_t)w * 8);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if ((tile + 1) * G::T > seq_len) {
+        // the tile reaches past seq_len: zero V of the keys beyond it
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int u = tid + it * NT;
+            const int p = u / G::UPP;
+            const int w = u % G::UPP;
+            vv[it] = mask_tokens(vv[it], (w & 1) * 8, seq_len - (tile * G::NKB + p) * BS);
+        }
+    }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int u = tid + it * NT;
         const int p = u / G::UPP;
         const int w = u % G::UPP;
-        const int valid = seq_len - (tile * G::NKB + p) * BS;
-        const u32x4 v = valid >= BS ? vv[it] : mask_tokens(vv[it], (w & 1) * 8, valid);
         const int du = w >> 4, tok = w & 15;
         *reinterpret_cast<u32x4 *>(kl + p * G::PAGE + (du * 16 + ksw(tok, p)) * 16) = kv[it];
         const int d = w >> 1, half = w & 1;
-        *reinterpret_cast<u32x4 *>(vl + p * G::PAGE + (d * 2 + vsw(half, d)) * 16) = v;
+        *reinterpret_cast<u32x4 *>(vl + p * G::PAGE + (d * 2 + vsw(half, d)) * 16) = vv[it];
     }
 }
 
@@ -213,8 +243,7 @@ __device__ __forceinline__ void tile_scores(const char *lds, const Cols<D> &col,
             mx = fmax2(mx, s[kb][i]);
         }
     }
-    mx = fmax2(mx, wave_xor(mx, 16));
-    mx = fmax2(mx, wave_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float mu = mx == -INFINITY ? 0.f : mx;
 
     // p = exp2(t - m); l in a fixed tree: pairs inside a block, blocks pairwise
@@ -232,8 +261,7 @@ __device__ __forceinline__ void tile_scores(const char *lds, const Cols<D> &col,
         for (int kb = 0; kb < G::NKB; kb += 2 * w)
             part[kb] = __fadd_rn(part[kb], part[kb + w]);
     float l = part[0];
-    l = __fadd_rn(l, wave_xor(l, 16));
-    l = __fadd_rn(l, wave_xor(l, 32));
+    l = sum_xor32(sum_xor16(l));
     o.m = mx;
     o.l = l;
 
@@ -406,12 +434,58 @@ __device__ __forceinline__ bool row_ok(const AttnArgs &a, int b, int &q0, int &q
 // different column blocks are interleaved, each K / V fragment read from LDS
 // once for all CB blocks, and fragment reads are software-pipelined one
 // step ahead (scheduling barriers keep the compiler from hoisting every read
-// to the top, which would multiply the register footprint).  need_mask is
-// false when every column of the wave sees every key of the tile; the
+// to the top, which would multiply the register footprint).  MASK is false
+// when every column of the wave sees every key of the tile; the
 // multiply-only path then gives the same values as the masked one.
-template <int D, int CB>
+// P.V for every 16-dim block of CB column blocks, each result folded into
+// its state at once.  GENERAL selects fold1's full form (some column's max
+// grew this tile); otherwise every column takes the fma(acc, f, ACC) branch,
+// which fold1 would pick anyway -- the same values without the selects.
+template <int D, int CB, bool GENERAL>
+__device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS], const float (&f)[CB],
+                                           const bool (&up)[CB], State<D> (&st)[CB])
+{
+    using G = Geo<D>;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    auto vaddr = [&](int db) -> const char * {
+        const int d = 16 * db + c;
+        return vl + (g >> 1) * G::PAGE + (d * 2 + vsw(g & 1, d)) * 16;
+    };
+    // V fragments are read just in time (the second wave on the SIMD covers
+    // the LDS latency); reading one block ahead costs more registers than
+    // two waves per SIMD can spare.
+    bf16x8 vf[G::NKS];
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+        {
+            const char *pn = vaddr(db);
+#pragma unroll
+            for (int stp = 0; stp < G::NKS; ++stp)
+                vf[stp] = *reinterpret_cast<const bf16x8 *>(pn + 2 * stp * G::PAGE);
+        }
+        f32x4 acc[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int stp = 0; stp < G::NKS; ++stp)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[stp], pf[cb][stp], acc[cb], 0, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                st[cb].acc[db][i] = GENERAL ? fold1v(st[cb].acc[db][i], acc[cb][i], f[cb], up[cb])
+                                            : __builtin_fmaf(acc[cb][i], f[cb], st[cb].acc[db][i]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int D, int CB, bool MASK>
 __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&cols)[CB], int tile, float scale_log2,
-                                             State<D> (&st)[CB], bool need_mask)
+                                             State<D> (&st)[CB])
 {
     using G = Geo<D>;
     const int lane = threadIdx.x & 63;
@@ -460,37 +534,36 @@ __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&co
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- softmax statistics and P^T per column block
+    // ---- softmax statistics and P^T, each step for all column blocks
     const int key0 = tile * G::T;
     float mx[CB], lsum[CB];
     bf16x8 pf[CB][G::NKS];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         float m = -INFINITY;
-        if (need_mask) {
 #pragma unroll
-            for (int kb = 0; kb < G::NKB; ++kb) {
-                const int stp = kb >> 1, e = kb & 1;
+        for (int kb = 0; kb < G::NKB; ++kb) {
+            const int stp = kb >> 1, e = kb & 1;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i) {
+                const float t = __fmul_rn(s[cb][kb][i], scale_log2);
+                if (MASK) {
                     const int key = key0 + 32 * stp + 8 * g + 4 * e + i;
-                    const float t = __fmul_rn(s[cb][kb][i], scale_log2);
                     s[cb][kb][i] = key < cols[cb].lim ? t : -INFINITY;
-                    m = fmax2(m, s[cb][kb][i]);
+                } else {
+                    s[cb][kb][i] = t;
                 }
+                m = fmax2(m, s[cb][kb][i]);
             }
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < G::NKB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    s[cb][kb][i] = __fmul_rn(s[cb][kb][i], scale_log2);
-                    m = fmax2(m, s[cb][kb][i]);
-                }
         }
-        m = fmax2(m, wave_xor(m, 16));
-        m = fmax2(m, wave_xor(m, 32));
-        const float mu = m == -INFINITY ? 0.f : m;
+        mx[cb] = m;
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        mx[cb] = max_xor32(max_xor16(mx[cb]));
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const float mu = mx[cb] == -INFINITY ? 0.f : mx[cb];
         float part[G::NKB];
 #pragma unroll
         for (int kb = 0; kb < G::NKB; ++kb) {
@@ -504,11 +577,7 @@ __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&co
 #pragma unroll
             for (int kb = 0; kb < G::NKB; kb += 2 * w)
                 part[kb] = __fadd_rn(part[kb], part[kb + w]);
-        float l = part[0];
-        l = __fadd_rn(l, wave_xor(l, 16));
-        l = __fadd_rn(l, wave_xor(l, 32));
-        mx[cb] = m;
-        lsum[cb] = l;
+        lsum[cb] = part[0];
 #pragma unroll
         for (int stp = 0; stp < G::NKS; ++stp)
 #pragma unroll
@@ -517,53 +586,25 @@ __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&co
                 pf[cb][stp][4 + i] = (__bf16)s[cb][2 * stp + 1][i];
             }
     }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        lsum[cb] = sum_xor32(sum_xor16(lsum[cb]));
 
-    // ---- fold factors
+    // ---- fold factors; one wave-uniform choice of fold sequence per tile
     float f[CB];
-    bool up[CB], any_up[CB];
+    bool up[CB];
+    bool any_up = false;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         f[cb] = fold_factor(st[cb].M, mx[cb], up[cb]);
-        any_up[cb] = __ballot(up[cb]) != 0;
+        any_up |= __ballot(up[cb]) != 0;
     }
 
     // ---- O^T = V^T . P^T per 16-dim block, folded straight into the states
-    auto vaddr = [&](int db) -> const char * {
-        const int d = 16 * db + c;
-        return vl + (g >> 1) * G::PAGE + (d * 2 + vsw(g & 1, d)) * 16;
-    };
-    bf16x8 vf[G::NKS], vn[G::NKS];
-    {
-        const char *p0 = vaddr(0);
-#pragma unroll
-        for (int stp = 0; stp < G::NKS; ++stp)
-            vf[stp] = *reinterpret_cast<const bf16x8 *>(p0 + 2 * stp * G::PAGE);
-    }
-#pragma unroll
-    for (int db = 0; db < G::NDB; ++db) {
-        if (db + 1 < G::NDB) {
-            const char *pn = vaddr(db + 1);
-#pragma unroll
-            for (int stp = 0; stp < G::NKS; ++stp)
-                vn[stp] = *reinterpret_cast<const bf16x8 *>(pn + 2 * stp * G::PAGE);
-        }
-        f32x4 acc[CB];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-            acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int stp = 0; stp < G::NKS; ++stp)
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[stp], pf[cb][stp], acc[cb], 0, 0, 0);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-            fold_acc(st[cb].acc[db], acc[cb], f[cb], up[cb], any_up[cb]);
-#pragma unroll
-        for (int stp = 0; stp < G::NKS; ++stp)
-            vf[stp] = vn[stp];
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    if (any_up)
+        prefill_pv<D, CB, true>(vl, pf, f, up, st);
+    else
+        prefill_pv<D, CB, false>(vl, pf, f, up, st);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
         fold_stats(st[cb].M, st[cb].L, mx[cb], lsum[cb], f[cb], up[cb]);
@@ -633,12 +674,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 512 ? 1
         stage_tile<D>(lds, a, bt_row, seq_len, kvh, tile);
         __syncthreads();
         if (active)
-            prefill_tile<D, CB>(lds, cols, tile, a.scale_log2, st, (tile + 1) * G::T > min_lim);
+        {
+            if ((tile + 1) * G::T > min_lim)
+                prefill_tile<D, CB, true>(lds, cols, tile, a.scale_log2, st);
+            else
+                prefill_tile<D, CB, false>(lds, cols, tile, a.scale_log2, st);
+        }
     }
+    // column bookkeeping is recomputed here rather than kept live in the loop
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-        if (ci[cb].lim > 0)
-            store_out<D>(a, ci[cb], st[cb]);
+    for (int cb = 0; cb < CB; ++cb) {
+        const ColInfo cj = col_info(a, cg * NCOL + (wave * CB + cb) * 16 + c, kvh, q0, q_len, seq_len);
+        if (cj.lim > 0)
+            store_out<D>(a, cj, st[cb]);
+    }
 }
 
 // ---------------------------------------------------------------- split-KV (decode)
@@ -740,8 +789,7 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
             mx = fmax2(mx, s[kl][i]);
         }
     }
-    mx = fmax2(mx, wave_xor(mx, 16));
-    mx = fmax2(mx, wave_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     if (g == 0)
         smax[w][c] = mx;
     __syncthreads();
@@ -768,8 +816,7 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
 
     // ---- l: remaining levels of the tree, then across lanes
     float l = __fadd_rn(__fadd_rn(ssum[0][lane], ssum[1][lane]), __fadd_rn(ssum[2][lane], ssum[3][lane]));
-    l = __fadd_rn(l, wave_xor(l, 16));
-    l = __fadd_rn(l, wave_xor(l, 32));
+    l = sum_xor32(sum_xor16(l));
 
     // ---- P^T operands of every 32-key step, then P.V for this wave's dims
     bf16x8 pf[G::NKS];
@@ -922,6 +969,148 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
     }
 }
 
+// ---------------------------------------------------------------- double-buffered prefill
+
+// Same column/tile work as prefill_kernel, for large grids: a workgroup of 8
+// waves (256 columns) owns one CU and two K/V tile buffers in LDS.  Tile t+1
+// is fetched straight from HBM into the idle buffer (global_load_lds: lane L
+// of a wave writes 16 bytes at the wave's LDS base + 16 L, so each lane
+// loads the unit that belongs at its swizzled slot) while tile t is
+// computed; no staging registers, no wait for data between tiles.  V of keys
+// at or beyond seq_len is zeroed in LDS once the tail tile has landed.
+constexpr int DB_WAVES = 8;
+constexpr int DB_NT = DB_WAVES * 64;
+
+template <int D>
+__device__ __forceinline__ void db_issue_tile(char *buf, const AttnArgs &a, const int32_t *bt_row, int kvh, int tile)
+{
+    using G = Geo<D>;
+    static_assert(G::PAGE % 1024 == 0, "page = whole 1 KB wave chunks");
+    constexpr int CPP = G::PAGE / 1024;            // 1 KB chunks per page
+    constexpr int CHUNKS = G::NKB * CPP;           // per K (or V) tile
+    static_assert(CHUNKS % DB_WAVES == 0, "chunks split evenly over waves");
+    const ids_t<G::NKB> blk = tile_blocks<G::NKB>(a, bt_row, tile);
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t hoff = (int64_t)kvh * BS * D;
+#pragma unroll
+    for (int i = 0; i < CHUNKS / DB_WAVES; ++i) {
+        const int ch = w + DB_WAVES * i;
+        const int pg = ch / CPP;
+        const int slot = (ch % CPP) * 64 + lane;   // 16-byte unit within the page
+        const int64_t b = (int64_t)blk[pg];
+        // K: slot = (du, tok'), global unit (du, ksw(tok', pg))
+        const int du = slot >> 4, tk = ksw(slot & 15, pg);
+        __builtin_amdgcn_global_load_lds(a.k_cache + b * a.k_block_stride + hoff + (du * 16 + tk) * 8,
+                                         (__attribute__((address_space(3))) void *)(buf + pg * G::PAGE + (slot - lane) * 16),
+                                         16, 0, 0);
+        // V: slot = (d, half'), global unit (d, vsw(half', d))
+        const int d = slot >> 1, hf = vsw(slot & 1, d);
+        __builtin_amdgcn_global_load_lds(a.v_cache + b * a.v_block_stride + hoff + (d * 2 + hf) * 8,
+                                         (__attribute__((address_space(3))) void *)(buf + G::NKB * G::PAGE + pg * G::PAGE +
+                                                                                    (slot - lane) * 16),
+                                         16, 0, 0);
+    }
+}
+
+// Zero V of keys >= seq_len in a staged tile (only the tile holding seq_len - 1
+// and later ones can have such keys).
+template <int D>
+__device__ __forceinline__ void db_mask_tail(char *buf, int seq_len, int tile)
+{
+    using G = Geo<D>;
+    char *vl = buf + G::NKB * G::PAGE;
+    for (int u = threadIdx.x; u < G::NKB * G::UPP; u += DB_NT) {
+        const int pg = u / G::UPP, slot = u % G::UPP;
+        const int valid = seq_len - (tile * G::NKB + pg) * BS;
+        if (valid >= BS)
+            continue;
+        const int d = slot >> 1, hf = vsw(slot & 1, d);
+        u32x4 *q = reinterpret_cast<u32x4 *>(vl + pg * G::PAGE + slot * 16);
+        *q = mask_tokens(*q, hf * 8, valid);
+    }
+}
+
+template <int D, int CB>
+__global__ __launch_bounds__(DB_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_db_kernel(AttnArgs a)
+{
+    using G = Geo<D>;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    constexpr int NCOL = DB_WAVES * CB * 16;
+    constexpr int TILE_BYTES = G::LDS;            // K + V of one tile
+
+    const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
+    const int per = (n + 7) / 8;
+    const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (j >= n)
+        return;
+    const int cgi = j % a.col_groups;
+    const int kvh = (j / a.col_groups) % a.num_kv_heads;
+    const int b = j / (a.col_groups * a.num_kv_heads);
+    const int cg = a.col_groups - 1 - cgi;
+
+    int q0, q_len, seq_len;
+    if (!row_ok(a, b, q0, q_len, seq_len))
+        return;
+    const int ncols = q_len * a.group;
+    if (cg * NCOL >= ncols)
+        return;
+    const int col_last = min((cg + 1) * NCOL, ncols) - 1;
+    const int pos_last = seq_len - q_len + col_last / a.group;
+    const int last_tile = (a.causal ? pos_last : seq_len - 1) / G::T;
+    const int32_t *bt_row = a.block_tables + (int64_t)b * a.bt_stride;
+
+    const int wave = threadIdx.x >> 6;
+    const int c = threadIdx.x & 15;
+    Cols<D> cols[CB];
+    ColInfo ci[CB];
+    State<D> st[CB];
+    bool active = false;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int col = cg * NCOL + (wave * CB + cb) * 16 + c;
+        ci[cb] = col_info(a, col, kvh, q0, q_len, seq_len);
+        load_q<D>(cols[cb], a, ci[cb]);
+        state_init<D>(st[cb]);
+        active |= (cg * NCOL + (wave * CB + cb) * 16) < ncols;
+    }
+    int min_lim = 0x7fffffff;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        min_lim = min(min_lim, cols[cb].lim);
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2)
+        min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
+
+    db_issue_tile<D>(lds, a, bt_row, kvh, 0);
+    for (int tile = 0; tile <= last_tile; ++tile) {
+        char *cur = lds + (tile & 1) * TILE_BYTES;
+        // this thread's loads of `tile` have landed; after the barrier every
+        // wave's have, and nobody still reads the other buffer
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if ((tile + 1) * G::T > seq_len) {
+            db_mask_tail<D>(cur, seq_len, tile);
+            __syncthreads();
+        }
+        if (tile < last_tile)
+            db_issue_tile<D>(lds + ((tile + 1) & 1) * TILE_BYTES, a, bt_row, kvh, tile + 1);
+        if (active)
+        {
+            if ((tile + 1) * G::T > min_lim)
+                prefill_tile<D, CB, true>(cur, cols, tile, a.scale_log2, st);
+            else
+                prefill_tile<D, CB, false>(cur, cols, tile, a.scale_log2, st);
+        }
+    }
+    // column bookkeeping is recomputed here rather than kept live in the loop
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const ColInfo cj = col_info(a, cg * NCOL + (wave * CB + cb) * 16 + c, kvh, q0, q_len, seq_len);
+        if (cj.lim > 0)
+            store_out<D>(a, cj, st[cb]);
+    }
+}
+
 }  // namespace
 
 template <int D, int CB>
@@ -943,11 +1132,36 @@ static hipError_t prefill_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, in
     return hipGetLastError();
 }
 
+template <int D, int CB>
+static hipError_t prefill_db_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
+{
+    constexpr int NCOL = DB_WAVES * CB * 16;
+    a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
+    const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;
+    const int64_t grid = (n + 7) / 8 * 8;
+    if (grid <= 0)
+        return hipSuccess;
+    if (grid > 0x7fffffff)
+        return hipErrorInvalidValue;
+    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_db_kernel<D, CB>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Geo<D>::LDS);
+    (void)attr;
+    hipLaunchKernelGGL((prefill_db_kernel<D, CB>), dim3((unsigned)grid), dim3(DB_NT), 2 * Geo<D>::LDS, s, a);
+    *blocks = (uint64_t)grid;
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks)
 {
     const int mq = max_query_len;
+    // Double-buffered 8-wave kernel when it still yields a workgroup per CU
+    // (256 CUs); the 4-wave kernel keeps small grids spread over the chip.
+    const int64_t db_groups = (int64_t)a.num_seqs * a.num_kv_heads * ((mq * a.group + 255) / 256);
     switch (head_dim) {
-    case 128: return prefill_launch<128, 2>(a, s, blocks, mq);
+    case 128:
+        if (db_groups >= 256)
+            return prefill_db_launch<128, 2>(a, s, blocks, mq);
+        return prefill_launch<128, 2>(a, s, blocks, mq);
     case 256: return prefill_launch<256, 1>(a, s, blocks, mq);
     case 512: return prefill_launch<512, 1>(a, s, blocks, mq);
     default: return hipErrorInvalidValue;

@@ -164,7 +164,8 @@ int kvp_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
  *                    q[query_start_loc[b] .. query_start_loc[b+1]); they sit
  *                    at the last q_len positions of the row (bottom-right).
  *   max_query_len, max_seq_len  host bounds of the device metadata (no sync).
- *   scale            softmax scale applied to q.k.
+ *   scale            softmax scale applied to q.k; positive and finite
+ *                    (the kernels take the max of the unscaled scores).
  *   causal           1: query at position p sees keys 0..p; 0: all keys.
  * Query head h reads kv head h / (num_q_heads / num_kv_heads).
  * Rows with q_len == 0 are skipped; rows that violate 0 <= q_len <=

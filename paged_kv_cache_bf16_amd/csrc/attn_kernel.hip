@@ -76,7 +76,10 @@ __device__ __forceinline__ int vsw(int half, int d)
     return half ^ (((d >> 2) ^ (d >> 3)) & 1);
 }
 
-__device__ __forceinline__ float fmax2(float a, float b) { return a > b ? a : b; }
+// IEEE 754-2019 maximum (v_maximum3_f32 for nested uses; unlike fmaxf it
+// needs no quieting step on operands such as MFMA results).  Maxima are
+// exact in any order and -0 < +0, so every kernel gets the same bits.
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // Cross-lane steps of the softmax reductions, lane l combined with lane
 // l ^ 16, then with lane l ^ 32, using the gfx950 row / half swaps (VALU, no
@@ -97,12 +100,12 @@ __device__ __forceinline__ float sum_xor32(float v)
 __device__ __forceinline__ float max_xor16(float v)
 {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float v)
 {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // ---------------------------------------------------------------- staging
@@ -195,164 +198,68 @@ struct Cols {
     int lim;         // keys < lim are visible (0: column inactive)
 };
 
-// Softmax statistics and BF16 probabilities of one tile for one column block.
-template <int D>
-struct Scores {
-    float m, l;                       // tile max (scaled, log2 domain) and sum of p
-    bf16x8 pf[Geo<D>::NKS];           // P^T operands, one per 32-key PV step
-};
-
-// Scores and softmax statistics of one tile for one column block.
-template <int D>
-__device__ __forceinline__ void tile_scores(const char *lds, const Cols<D> &col, int tile,
-                                            float scale_log2, Scores<D> &o)
-{
-    using G = Geo<D>;
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4, c = lane & 15;
-    const char *kl = lds;
-
-    // S^T = K . Q^T, one 16-key block at a time, head dim ascending
-    f32x4 s[G::NKB];
-#pragma unroll
-    for (int kb = 0; kb < G::NKB; ++kb) {
-        const int st = kb >> 1, e = kb & 1;
-        const int page = 2 * st + (c >> 3);
-        const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
-        const char *rowp = kl + page * G::PAGE + ksw(tok, page) * 16;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < G::NDS; ++ds) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(rowp + (4 * ds + g) * 256);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, col.qf[ds], acc, 0, 0, 0);
-        }
-        s[kb] = acc;
-    }
-
-    // scale, mask, max
-    const int key0 = tile * G::T;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < G::NKB; ++kb) {
-        const int st = kb >> 1, e = kb & 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 32 * st + 8 * g + 4 * e + i;
-            const float t = __fmul_rn(s[kb][i], scale_log2);
-            s[kb][i] = key < col.lim ? t : -INFINITY;
-            mx = fmax2(mx, s[kb][i]);
-        }
-    }
-    mx = max_xor32(max_xor16(mx));
-    const float mu = mx == -INFINITY ? 0.f : mx;
-
-    // p = exp2(t - m); l in a fixed tree: pairs inside a block, blocks pairwise
-    float part[G::NKB];
-#pragma unroll
-    for (int kb = 0; kb < G::NKB; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            s[kb][i] = __builtin_amdgcn_exp2f(__fsub_rn(s[kb][i], mu));
-        part[kb] = __fadd_rn(__fadd_rn(s[kb][0], s[kb][1]), __fadd_rn(s[kb][2], s[kb][3]));
-    }
-#pragma unroll
-    for (int w = 1; w < G::NKB; w *= 2)
-#pragma unroll
-        for (int kb = 0; kb < G::NKB; kb += 2 * w)
-            part[kb] = __fadd_rn(part[kb], part[kb + w]);
-    float l = part[0];
-    l = sum_xor32(sum_xor16(l));
-    o.m = mx;
-    o.l = l;
-
-    // P^T operands: step st = keys 32st + 8g + 0..7 = block 2st (i) then 2st+1 (i)
-#pragma unroll
-    for (int st = 0; st < G::NKS; ++st)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            o.pf[st][i] = (__bf16)s[2 * st][i];
-            o.pf[st][4 + i] = (__bf16)s[2 * st + 1][i];
-        }
-}
-
-// O^T = V^T . P^T for each 16-dim block, keys ascending in 32-key steps;
-// sink(db, acc) receives dims 16*db + 4*g + 0..3 of the lane's column.
-template <int D, typename Sink>
-__device__ __forceinline__ void tile_pv(const char *lds, const Scores<D> &sc, Sink &&sink)
-{
-    using G = Geo<D>;
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4, c = lane & 15;
-    const char *vl = lds + G::NKB * G::PAGE;
-#pragma unroll
-    for (int db = 0; db < G::NDB; ++db) {
-        const int d = 16 * db + c;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < G::NKS; ++st) {
-            const int page = 2 * st + (g >> 1);
-            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vl + page * G::PAGE + (d * 2 + vsw(g & 1, d)) * 16);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, sc.pf[st], acc, 0, 0, 0);
-        }
-        sink(db, acc);
-    }
-}
-
-// Running softmax state of one column (lane-replicated over g).
+// Running softmax state of one column (lane-replicated over g).  ACC and L
+// are kept relative to the reference R: the running maximum rounded up to a
+// multiple of kRefStep (log2 units).  R changes only when the running
+// maximum crosses such a multiple, so nearly every tile folds with one FMA
+// per value and no rescaling of ACC.
 template <int D>
 struct State {
-    float M, L;
+    float R, L;
     f32x4 acc[Geo<D>::NDB];
 };
 
 template <int D>
 __device__ __forceinline__ void state_init(State<D> &st)
 {
-    st.M = -INFINITY;
+    st.R = -INFINITY;
     st.L = 0.f;
 #pragma unroll
     for (int db = 0; db < Geo<D>::NDB; ++db)
         st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Fold factor for folding a tile with max m into a state with max M:
-// up = (m > M); f = exp2(M - m) if up else exp2(m - M); 0 for an empty tile.
-__device__ __forceinline__ float fold_factor(float M, float m, bool &up)
+constexpr float kRefStep = 16.f;
+
+// Reference of a maximum: m rounded up to a multiple of kRefStep (exact;
+// monotone, so the reference of a running max is the max of the references).
+__device__ __forceinline__ float ref_of(float m)
 {
-    up = m > M;
-    const float f = up ? __builtin_amdgcn_exp2f(__fsub_rn(M, m)) : __builtin_amdgcn_exp2f(__fsub_rn(m, M));
-    return m == -INFINITY ? 0.f : f;
+    return __fmul_rn(__builtin_ceilf(__fmul_rn(m, 1.f / kRefStep)), kRefStep);
 }
 
-// acc' = up ? fma(acc, f, tile) : fma(tile, f, acc)
-__device__ __forceinline__ float fold1v(float acc, float tile, float f, bool up)
+// Factors for folding a tile with max m (log2 units, -inf when empty) into
+// a state with reference R.  Rn = max(R, ref(m)); up = Rn > R;
+// g = exp2(R - Rn) rescales the state (used only when up);
+// h = exp2(m - Rn) scales the tile, 0 for an empty tile.
+struct FoldF {
+    float g, h, Rn;
+    bool up;
+};
+
+__device__ __forceinline__ FoldF fold_factors(float R, float m)
 {
-    const float x = up ? acc : tile;
-    const float y = up ? tile : acc;
-    return __builtin_fmaf(x, f, y);
+    FoldF f;
+    f.Rn = fmax2(R, ref_of(m));
+    f.up = f.Rn > R;
+    f.g = __builtin_amdgcn_exp2f(__fsub_rn(R, f.Rn));
+    f.h = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__fsub_rn(m, f.Rn));
+    return f;
 }
 
-__device__ __forceinline__ void fold1(float &acc, float tile, float f, bool up) { acc = fold1v(acc, tile, f, up); }
-
-// fold1 on four dims.  any_up (wave-uniform) only selects a cheaper
-// instruction sequence for the common case; the results are identical.
-__device__ __forceinline__ void fold_acc(f32x4 &acc, const f32x4 &tile, float f, bool up, bool any_up)
+// ACC' = up ? fma(ACC, g, tile * h) : fma(tile, h, ACC)
+__device__ __forceinline__ float fold1v(float acc, float tile, float g, float h, bool up)
 {
-    if (!any_up) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc[i] = __builtin_fmaf(tile[i], f, acc[i]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc[i] = fold1v(acc[i], tile[i], f, up);
-    }
+    const float rescaled = __builtin_fmaf(acc, g, __fmul_rn(tile, h));
+    const float plain = __builtin_fmaf(tile, h, acc);
+    return up ? rescaled : plain;
 }
 
-__device__ __forceinline__ void fold_stats(float &M, float &L, float m, float l, float f, bool up)
+// (R, L) after the fold; L follows the same rule as ACC.
+__device__ __forceinline__ void fold_stats(float &R, float &L, float l, const FoldF &f)
 {
-    L = up ? __builtin_fmaf(L, f, l) : __builtin_fmaf(l, f, L);
-    M = up ? m : M;
+    L = fold1v(L, l, f.g, f.h, f.up);
+    R = f.Rn;
 }
 
 // bf16 output of one dim: RNE of acc * (1 / L), signed zero made +0
@@ -429,21 +336,22 @@ __device__ __forceinline__ bool row_ok(const AttnArgs &a, int b, int &q0, int &q
 // ---------------------------------------------------------------- joint tile step (prefill)
 
 // One tile for CB column blocks of a wave, folded into their states.  Per
-// column this is exactly tile_scores + tile_pv + the fold (same MFMA chains,
-// same softmax operations and tree, same fold); only independent chains of
-// different column blocks are interleaved, each K / V fragment read from LDS
+// column these are exactly the operations of the fixed schedule (the same
+// MFMA chains, softmax operations and sum tree, and fold as the split-KV
+// kernel); only independent chains of different column blocks are interleaved, each K / V fragment read from LDS
 // once for all CB blocks, and fragment reads are software-pipelined one
 // step ahead (scheduling barriers keep the compiler from hoisting every read
 // to the top, which would multiply the register footprint).  MASK is false
 // when every column of the wave sees every key of the tile; the
 // multiply-only path then gives the same values as the masked one.
 // P.V for every 16-dim block of CB column blocks, each result folded into
-// its state at once.  GENERAL selects fold1's full form (some column's max
-// grew this tile); otherwise every column takes the fma(acc, f, ACC) branch,
-// which fold1 would pick anyway -- the same values without the selects.
+// its state at once.  GENERAL selects fold1v's full form (some column's
+// reference moved this tile); otherwise every column takes the plain
+// fma(tile, h, ACC) branch, which fold1v would pick anyway -- the same
+// values without the selects.
 template <int D, int CB, bool GENERAL>
-__device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS], const float (&f)[CB],
-                                           const bool (&up)[CB], State<D> (&st)[CB])
+__device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS],
+                                           const FoldF (&f)[CB], State<D> (&st)[CB])
 {
     using G = Geo<D>;
     const int lane = threadIdx.x & 63;
@@ -477,8 +385,8 @@ __device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                st[cb].acc[db][i] = GENERAL ? fold1v(st[cb].acc[db][i], acc[cb][i], f[cb], up[cb])
-                                            : __builtin_fmaf(acc[cb][i], f[cb], st[cb].acc[db][i]);
+                st[cb].acc[db][i] = GENERAL ? fold1v(st[cb].acc[db][i], acc[cb][i], f[cb].g, f[cb].h, f[cb].up)
+                                            : __builtin_fmaf(acc[cb][i], f[cb].h, st[cb].acc[db][i]);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -534,42 +442,46 @@ __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&co
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- softmax statistics and P^T, each step for all column blocks
+    // ---- softmax statistics and P^T, each step for all column blocks.
+    // The max runs over raw scores (scale_log2 > 0, so max(S) * scale_log2
+    // is the max of the scaled scores); p = exp2(fma(S, scale_log2, -m)).
     const int key0 = tile * G::T;
     float mx[CB], lsum[CB];
     bf16x8 pf[CB][G::NKS];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        float m = -INFINITY;
+        float mk[G::NKB];
 #pragma unroll
         for (int kb = 0; kb < G::NKB; ++kb) {
-            const int stp = kb >> 1, e = kb & 1;
+            if (MASK) {
+                const int stp = kb >> 1, e = kb & 1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float t = __fmul_rn(s[cb][kb][i], scale_log2);
-                if (MASK) {
+                for (int i = 0; i < 4; ++i) {
                     const int key = key0 + 32 * stp + 8 * g + 4 * e + i;
-                    s[cb][kb][i] = key < cols[cb].lim ? t : -INFINITY;
-                } else {
-                    s[cb][kb][i] = t;
+                    s[cb][kb][i] = key < cols[cb].lim ? s[cb][kb][i] : -INFINITY;
                 }
-                m = fmax2(m, s[cb][kb][i]);
             }
+            mk[kb] = fmax2(fmax2(s[cb][kb][0], s[cb][kb][1]), fmax2(s[cb][kb][2], s[cb][kb][3]));
         }
-        mx[cb] = m;
+#pragma unroll
+        for (int w = 1; w < G::NKB; w *= 2)
+#pragma unroll
+            for (int kb = 0; kb < G::NKB; kb += 2 * w)
+                mk[kb] = fmax2(mk[kb], mk[kb + w]);
+        mx[cb] = mk[0];
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
-        mx[cb] = max_xor32(max_xor16(mx[cb]));
+        mx[cb] = __fmul_rn(max_xor32(max_xor16(mx[cb])), scale_log2);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        const float mu = mx[cb] == -INFINITY ? 0.f : mx[cb];
+        const float nmu = mx[cb] == -INFINITY ? 0.f : -mx[cb];
         float part[G::NKB];
 #pragma unroll
         for (int kb = 0; kb < G::NKB; ++kb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                s[cb][kb][i] = __builtin_amdgcn_exp2f(__fsub_rn(s[cb][kb][i], mu));
+                s[cb][kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][kb][i], scale_log2, nmu));
             part[kb] = __fadd_rn(__fadd_rn(s[cb][kb][0], s[cb][kb][1]), __fadd_rn(s[cb][kb][2], s[cb][kb][3]));
         }
 #pragma unroll
@@ -591,23 +503,22 @@ __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&co
         lsum[cb] = sum_xor32(sum_xor16(lsum[cb]));
 
     // ---- fold factors; one wave-uniform choice of fold sequence per tile
-    float f[CB];
-    bool up[CB];
+    FoldF f[CB];
     bool any_up = false;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        f[cb] = fold_factor(st[cb].M, mx[cb], up[cb]);
-        any_up |= __ballot(up[cb]) != 0;
+        f[cb] = fold_factors(st[cb].R, mx[cb]);
+        any_up |= __ballot(f[cb].up) != 0;
     }
 
     // ---- O^T = V^T . P^T per 16-dim block, folded straight into the states
     if (any_up)
-        prefill_pv<D, CB, true>(vl, pf, f, up, st);
+        prefill_pv<D, CB, true>(vl, pf, f, st);
     else
-        prefill_pv<D, CB, false>(vl, pf, f, up, st);
+        prefill_pv<D, CB, false>(vl, pf, f, st);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
-        fold_stats(st[cb].M, st[cb].L, mx[cb], lsum[cb], f[cb], up[cb]);
+        fold_stats(st[cb].R, st[cb].L, lsum[cb], f[cb]);
 }
 
 // ---------------------------------------------------------------- streaming prefill
@@ -784,17 +695,16 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = tile * G::T + 32 * st + 8 * g + 4 * e + i;
-            const float t = __fmul_rn(acc[i], a.scale_log2);
-            s[kl][i] = key < cols.lim ? t : -INFINITY;
-            mx = fmax2(mx, s[kl][i]);
+            s[kl][i] = key < cols.lim ? acc[i] : -INFINITY;
         }
+        mx = fmax2(mx, fmax2(fmax2(s[kl][0], s[kl][1]), fmax2(s[kl][2], s[kl][3])));
     }
     mx = max_xor32(max_xor16(mx));
     if (g == 0)
         smax[w][c] = mx;
     __syncthreads();
-    mx = fmax2(fmax2(smax[0][c], smax[1][c]), fmax2(smax[2][c], smax[3][c]));
-    const float mu = mx == -INFINITY ? 0.f : mx;
+    mx = __fmul_rn(fmax2(fmax2(smax[0][c], smax[1][c]), fmax2(smax[2][c], smax[3][c])), a.scale_log2);
+    const float nmu = mx == -INFINITY ? 0.f : -mx;
 
     // ---- p, this wave's level of the sum tree, P^T values to LDS
     float part[KPW];
@@ -802,7 +712,7 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     for (int kl = 0; kl < KPW; ++kl) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            s[kl][i] = __builtin_amdgcn_exp2f(__fsub_rn(s[kl][i], mu));
+            s[kl][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kl][i], a.scale_log2, nmu));
         part[kl] = __fadd_rn(__fadd_rn(s[kl][0], s[kl][1]), __fadd_rn(s[kl][2], s[kl][3]));
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -852,8 +762,9 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
 // every load of a round issued before any is used (the first round is
 // fetched before the row's length is even known: the workspace holds
 // max_tiles slots).  The fold factor of tile t depends only on the running
-// max before t -- the max of the earlier tile maxima, exact in any order --
-// so all factors come from one prefix-max scan; wave 0 then runs the
+// max before t -- the max of the earlier tile maxima, exact in any order,
+// whose reference is the state's reference -- so all factors come from one
+// prefix-max scan; wave 0 then runs the
 // dependent FMA chain in ascending tile order and writes the BF16 output.
 constexpr int kFoldSlice = 64;
 constexpr int kFoldTiles = 192;
@@ -899,7 +810,7 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
     using G = Geo<D>;
     constexpr int NSL = D / kFoldSlice;
     __shared__ float stage[kFoldTiles][kFoldSlice];
-    __shared__ float sm[kFoldTiles], sl[kFoldTiles], sf[kFoldTiles];
+    __shared__ float sm[kFoldTiles], sl[kFoldTiles], sg[kFoldTiles], sh[kFoldTiles];
     __shared__ int sup[kFoldTiles];
     __shared__ float wmax[NW];
 
@@ -941,27 +852,32 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
         if (lane == 63)
             wmax[w] = v;
         __syncthreads();
-        float pre = M;
-        for (int k = 0; k < w; ++k)
-            pre = fmax2(pre, wmax[k]);
+        float pre = M, total = M;
+        for (int k = 0; k < NW; ++k) {
+            pre = k < w ? fmax2(pre, wmax[k]) : pre;
+            total = fmax2(total, wmax[k]);
+        }
         const float incl = fmax2(pre, v);
         float excl = __shfl_up(incl, 1, 64);
         excl = lane == 0 ? pre : excl;
         if (th < nt) {
-            bool up;
-            sf[th] = fold_factor(excl, sm[th], up);
-            sup[th] = up;
+            const FoldF f = fold_factors(ref_of(excl), sm[th]);
+            sg[th] = f.g;
+            sh[th] = f.h;
+            sup[th] = f.up;
         }
         __syncthreads();
         if (th < kFoldSlice) {
 #pragma unroll 8
             for (int tt = 0; tt < nt; ++tt)
-                acc = fold1v(acc, stage[tt][th], sf[tt], sup[tt] != 0);
+                acc = fold1v(acc, stage[tt][th], sg[tt], sh[tt], sup[tt] != 0);
         }
-        // every thread carries (M, L): the next round's scan starts from M
+        // every thread carries (M, L): the next round's scan starts from M,
+        // the running max after this round
 #pragma unroll 8
         for (int tt = 0; tt < nt; ++tt)
-            fold_stats(M, L, sm[tt], sl[tt], sf[tt], sup[tt] != 0);
+            L = fold1v(L, sl[tt], sg[tt], sh[tt], sup[tt] != 0);
+        M = total;
     }
     if (th < kFoldSlice) {
         const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
@@ -978,12 +894,10 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
 // loads the unit that belongs at its swizzled slot) while tile t is
 // computed; no staging registers, no wait for data between tiles.  V of keys
 // at or beyond seq_len is zeroed in LDS once the tail tile has landed.
-constexpr int DB_WAVES = 8;
-constexpr int DB_NT = DB_WAVES * 64;
-
-template <int D>
+template <int D, int NWV>
 __device__ __forceinline__ void db_issue_tile(char *buf, const AttnArgs &a, const int32_t *bt_row, int kvh, int tile)
 {
+    constexpr int DB_WAVES = NWV;
     using G = Geo<D>;
     static_assert(G::PAGE % 1024 == 0, "page = whole 1 KB wave chunks");
     constexpr int CPP = G::PAGE / 1024;            // 1 KB chunks per page
@@ -1014,10 +928,11 @@ __device__ __forceinline__ void db_issue_tile(char *buf, const AttnArgs &a, cons
 
 // Zero V of keys >= seq_len in a staged tile (only the tile holding seq_len - 1
 // and later ones can have such keys).
-template <int D>
+template <int D, int NWV>
 __device__ __forceinline__ void db_mask_tail(char *buf, int seq_len, int tile)
 {
     using G = Geo<D>;
+    constexpr int DB_NT = NWV * 64;
     char *vl = buf + G::NKB * G::PAGE;
     for (int u = threadIdx.x; u < G::NKB * G::UPP; u += DB_NT) {
         const int pg = u / G::UPP, slot = u % G::UPP;
@@ -1030,12 +945,12 @@ __device__ __forceinline__ void db_mask_tail(char *buf, int seq_len, int tile)
     }
 }
 
-template <int D, int CB>
-__global__ __launch_bounds__(DB_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_db_kernel(AttnArgs a)
+template <int D, int CB, int NWV>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4))) void prefill_db_kernel(AttnArgs a)
 {
     using G = Geo<D>;
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    constexpr int NCOL = DB_WAVES * CB * 16;
+    constexpr int NCOL = NWV * CB * 16;
     constexpr int TILE_BYTES = G::LDS;            // K + V of one tile
 
     const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
@@ -1081,7 +996,7 @@ __global__ __launch_bounds__(DB_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     for (int off = 1; off < 64; off *= 2)
         min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
 
-    db_issue_tile<D>(lds, a, bt_row, kvh, 0);
+    db_issue_tile<D, NWV>(lds, a, bt_row, kvh, 0);
     for (int tile = 0; tile <= last_tile; ++tile) {
         char *cur = lds + (tile & 1) * TILE_BYTES;
         // this thread's loads of `tile` have landed; after the barrier every
@@ -1089,11 +1004,11 @@ __global__ __launch_bounds__(DB_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if ((tile + 1) * G::T > seq_len) {
-            db_mask_tail<D>(cur, seq_len, tile);
+            db_mask_tail<D, NWV>(cur, seq_len, tile);
             __syncthreads();
         }
         if (tile < last_tile)
-            db_issue_tile<D>(lds + ((tile + 1) & 1) * TILE_BYTES, a, bt_row, kvh, tile + 1);
+            db_issue_tile<D, NWV>(lds + ((tile + 1) & 1) * TILE_BYTES, a, bt_row, kvh, tile + 1);
         if (active)
         {
             if ((tile + 1) * G::T > min_lim)
@@ -1132,10 +1047,10 @@ static hipError_t prefill_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, in
     return hipGetLastError();
 }
 
-template <int D, int CB>
+template <int D, int CB, int NWV>
 static hipError_t prefill_db_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
 {
-    constexpr int NCOL = DB_WAVES * CB * 16;
+    constexpr int NCOL = NWV * CB * 16;
     a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
     const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;
     const int64_t grid = (n + 7) / 8 * 8;
@@ -1143,10 +1058,10 @@ static hipError_t prefill_db_launch(AttnArgs a, hipStream_t s, uint64_t *blocks,
         return hipSuccess;
     if (grid > 0x7fffffff)
         return hipErrorInvalidValue;
-    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_db_kernel<D, CB>,
+    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_db_kernel<D, CB, NWV>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Geo<D>::LDS);
     (void)attr;
-    hipLaunchKernelGGL((prefill_db_kernel<D, CB>), dim3((unsigned)grid), dim3(DB_NT), 2 * Geo<D>::LDS, s, a);
+    hipLaunchKernelGGL((prefill_db_kernel<D, CB, NWV>), dim3((unsigned)grid), dim3(NWV * 64), 2 * Geo<D>::LDS, s, a);
     *blocks = (uint64_t)grid;
     return hipGetLastError();
 }
@@ -1160,7 +1075,7 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
     switch (head_dim) {
     case 128:
         if (db_groups >= 256)
-            return prefill_db_launch<128, 2>(a, s, blocks, mq);
+            return prefill_db_launch<128, 2, 8>(a, s, blocks, mq);
         return prefill_launch<128, 2>(a, s, blocks, mq);
     case 256: return prefill_launch<256, 1>(a, s, blocks, mq);
     case 512: return prefill_launch<512, 1>(a, s, blocks, mq);

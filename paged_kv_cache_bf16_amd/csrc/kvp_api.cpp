@@ -251,8 +251,8 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
                     max_seq_len);
     if (causal != 0 && causal != 1)
         return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: causal must be 0 or 1");
-    if (!std::isfinite(scale))
-        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: scale must be finite");
+    if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(scale * 1.44269504088896340736f))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: scale must be positive and finite");
     if (num_seqs == 0 || max_query_len == 0)
         return ok();
     if (!q || !out || !block_tables || !seq_lens || !query_start_loc)

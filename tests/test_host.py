@@ -136,6 +136,9 @@ def _attn(lib, h, **kw):
     (dict(mq=200), kvp.KVP_ERR_INVALID_ARGUMENT),          # max_query_len > max_seq_len
     (dict(causal=2), kvp.KVP_ERR_INVALID_ARGUMENT),
     (dict(scale=float("nan")), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(scale=-0.1), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(scale=3e38), kvp.KVP_ERR_INVALID_ARGUMENT),
     (dict(ws=None), kvp.KVP_ERR_INVALID_ARGUMENT),
     (dict(wsb=64), kvp.KVP_ERR_WORKSPACE_TOO_SMALL),
     (dict(sl=None), kvp.KVP_ERR_INVALID_ARGUMENT),

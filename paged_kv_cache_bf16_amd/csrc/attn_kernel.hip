@@ -229,11 +229,11 @@ __device__ __forceinline__ float ref_of(float m)
 }
 
 // Factors for folding a tile with max m (log2 units, -inf when empty) into
-// a state with reference R.  Rn = max(R, ref(m)); up = Rn > R;
-// g = exp2(R - Rn) rescales the state (used only when up);
-// h = exp2(m - Rn) scales the tile, 0 for an empty tile.
+// a state with reference R.  Rn = max(R, ref(m)); gs = exp2(R - Rn) when
+// Rn > R (rescales the state), else 1; h = exp2(m - Rn) scales the tile,
+// 0 for an empty tile.
 struct FoldF {
-    float g, h, Rn;
+    float gs, h, Rn;
     bool up;
 };
 
@@ -242,23 +242,22 @@ __device__ __forceinline__ FoldF fold_factors(float R, float m)
     FoldF f;
     f.Rn = fmax2(R, ref_of(m));
     f.up = f.Rn > R;
-    f.g = __builtin_amdgcn_exp2f(__fsub_rn(R, f.Rn));
+    f.gs = f.up ? __builtin_amdgcn_exp2f(__fsub_rn(R, f.Rn)) : 1.f;
     f.h = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__fsub_rn(m, f.Rn));
     return f;
 }
 
-// ACC' = up ? fma(ACC, g, tile * h) : fma(tile, h, ACC)
-__device__ __forceinline__ float fold1v(float acc, float tile, float g, float h, bool up)
+// ACC' = fma(tile, h, ACC * gs).  ACC * 1 is exact, so a state whose
+// reference did not move may skip the product: the result is the same.
+__device__ __forceinline__ float fold1v(float acc, float tile, float gs, float h)
 {
-    const float rescaled = __builtin_fmaf(acc, g, __fmul_rn(tile, h));
-    const float plain = __builtin_fmaf(tile, h, acc);
-    return up ? rescaled : plain;
+    return __builtin_fmaf(tile, h, __fmul_rn(acc, gs));
 }
 
 // (R, L) after the fold; L follows the same rule as ACC.
 __device__ __forceinline__ void fold_stats(float &R, float &L, float l, const FoldF &f)
 {
-    L = fold1v(L, l, f.g, f.h, f.up);
+    L = fold1v(L, l, f.gs, f.h);
     R = f.Rn;
 }
 
@@ -345,11 +344,11 @@ __device__ __forceinline__ bool row_ok(const AttnArgs &a, int b, int &q0, int &q
 // when every column of the wave sees every key of the tile; the
 // multiply-only path then gives the same values as the masked one.
 // P.V for every 16-dim block of CB column blocks, each result folded into
-// its state at once.  GENERAL selects fold1v's full form (some column's
-// reference moved this tile); otherwise every column takes the plain
-// fma(tile, h, ACC) branch, which fold1v would pick anyway -- the same
-// values without the selects.
-template <int D, int CB, bool GENERAL>
+// its state with fma(tile, h, ACC) (the states were rescaled by gs first
+// where needed).  The V fragments of block db+1 are read while the MFMAs of
+// block db run, and block db is folded after the MFMAs of block db+1 are
+// issued, so neither the LDS latency nor the MFMA latency is exposed.
+template <int D, int CB>
 __device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS],
                                            const FoldF (&f)[CB], State<D> (&st)[CB])
 {
@@ -360,17 +359,21 @@ __device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB
         const int d = 16 * db + c;
         return vl + (g >> 1) * G::PAGE + (d * 2 + vsw(g & 1, d)) * 16;
     };
-    // V fragments are read just in time (the second wave on the SIMD covers
-    // the LDS latency); reading one block ahead costs more registers than
-    // two waves per SIMD can spare.
-    bf16x8 vf[G::NKS];
+    bf16x8 vf[G::NKS], vn[G::NKS];
+    {
+        const char *p0 = vaddr(0);
+#pragma unroll
+        for (int stp = 0; stp < G::NKS; ++stp)
+            vf[stp] = *reinterpret_cast<const bf16x8 *>(p0 + 2 * stp * G::PAGE);
+    }
+    f32x4 prev[CB];
 #pragma unroll
     for (int db = 0; db < G::NDB; ++db) {
-        {
-            const char *pn = vaddr(db);
+        if (db + 1 < G::NDB) {
+            const char *pn = vaddr(db + 1);
 #pragma unroll
             for (int stp = 0; stp < G::NKS; ++stp)
-                vf[stp] = *reinterpret_cast<const bf16x8 *>(pn + 2 * stp * G::PAGE);
+                vn[stp] = *reinterpret_cast<const bf16x8 *>(pn + 2 * stp * G::PAGE);
         }
         f32x4 acc[CB];
 #pragma unroll
@@ -381,14 +384,26 @@ __device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
                 acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[stp], pf[cb][stp], acc[cb], 0, 0, 0);
+        if (db > 0) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st[cb].acc[db - 1][i] = __builtin_fmaf(prev[cb][i], f[cb].h, st[cb].acc[db - 1][i]);
+        }
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
+            prev[cb] = acc[cb];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                st[cb].acc[db][i] = GENERAL ? fold1v(st[cb].acc[db][i], acc[cb][i], f[cb].g, f[cb].h, f[cb].up)
-                                            : __builtin_fmaf(acc[cb][i], f[cb].h, st[cb].acc[db][i]);
+        for (int stp = 0; stp < G::NKS; ++stp)
+            vf[stp] = vn[stp];
         __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st[cb].acc[G::NDB - 1][i] = __builtin_fmaf(prev[cb][i], f[cb].h, st[cb].acc[G::NDB - 1][i]);
 }
 
 template <int D, int CB, bool MASK>
@@ -511,11 +526,19 @@ __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&co
         any_up |= __ballot(f[cb].up) != 0;
     }
 
-    // ---- O^T = V^T . P^T per 16-dim block, folded straight into the states
-    if (any_up)
-        prefill_pv<D, CB, true>(vl, pf, f, st);
-    else
-        prefill_pv<D, CB, false>(vl, pf, f, st);
+    // ---- states whose reference moved are rescaled (ACC * 1 is exact, so
+    // every column of the wave may take the product); then O^T = V^T . P^T
+    // per 16-dim block, folded straight into the states
+    if (any_up) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st[cb].acc[db][i] = __fmul_rn(st[cb].acc[db][i], f[cb].gs);
+    }
+    prefill_pv<D, CB>(vl, pf, f, st);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
         fold_stats(st[cb].R, st[cb].L, lsum[cb], f[cb]);
@@ -811,7 +834,6 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
     constexpr int NSL = D / kFoldSlice;
     __shared__ float stage[kFoldTiles][kFoldSlice];
     __shared__ float sm[kFoldTiles], sl[kFoldTiles], sg[kFoldTiles], sh[kFoldTiles];
-    __shared__ int sup[kFoldTiles];
     __shared__ float wmax[NW];
 
     const int slice = blockIdx.x % NSL;
@@ -862,21 +884,20 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
         excl = lane == 0 ? pre : excl;
         if (th < nt) {
             const FoldF f = fold_factors(ref_of(excl), sm[th]);
-            sg[th] = f.g;
+            sg[th] = f.gs;
             sh[th] = f.h;
-            sup[th] = f.up;
         }
         __syncthreads();
         if (th < kFoldSlice) {
 #pragma unroll 8
             for (int tt = 0; tt < nt; ++tt)
-                acc = fold1v(acc, stage[tt][th], sg[tt], sh[tt], sup[tt] != 0);
+                acc = fold1v(acc, stage[tt][th], sg[tt], sh[tt]);
         }
         // every thread carries (M, L): the next round's scan starts from M,
         // the running max after this round
 #pragma unroll 8
         for (int tt = 0; tt < nt; ++tt)
-            L = fold1v(L, sl[tt], sg[tt], sh[tt], sup[tt] != 0);
+            L = fold1v(L, sl[tt], sg[tt], sh[tt]);
         M = total;
     }
     if (th < kFoldSlice) {

@@ -397,6 +397,9 @@ __device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB
 #pragma unroll
         for (int stp = 0; stp < G::NKS; ++stp)
             vf[stp] = vn[stp];
+        if (db + 1 < G::NDB)
+            __builtin_amdgcn_sched_group_barrier(0x100, G::NKS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, G::NKS * CB, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -454,6 +457,10 @@ __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&co
 #pragma unroll
         for (int ds = 0; ds < G::NDS; ++ds)
             kf[ds] = kn[ds];
+        // the next block's fragment reads go out before this block's MFMAs
+        if (kb + 1 < G::NKB)
+            __builtin_amdgcn_sched_group_barrier(0x100, G::NDS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, G::NDS * CB, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -913,37 +920,71 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
 // is fetched straight from HBM into the idle buffer (global_load_lds: lane L
 // of a wave writes 16 bytes at the wave's LDS base + 16 L, so each lane
 // loads the unit that belongs at its swizzled slot) while tile t is
-// computed; no staging registers, no wait for data between tiles.  V of keys
-// at or beyond seq_len is zeroed in LDS once the tail tile has landed.
-template <int D, int NWV>
-__device__ __forceinline__ void db_issue_tile(char *buf, const AttnArgs &a, const int32_t *bt_row, int kvh, int tile)
+// computed; no staging registers, no wait for data between tiles.  Wave w
+// stages page w of every tile (its K page and its V page, four 1 KB chunks
+// each); the page's block id is read two tiles ahead, so the id has landed
+// before the tile is issued.  V of keys at or beyond seq_len is zeroed in
+// LDS once the tail tile has landed.
+
+// Per-lane source byte offsets (inside one page) of the 16-byte units that
+// chunk 0 of page `page` holds at this lane's LDS slots; chunk i adds i KB
+// (the swizzles of K and V do not depend on the chunk).
+struct DbOffsets {
+    uint32_t k, v;
+};
+
+__device__ __forceinline__ DbOffsets db_offsets(int page)
 {
-    constexpr int DB_WAVES = NWV;
+    const int lane = threadIdx.x & 63;
+    DbOffsets o;
+    // K: slot (du, tok') holds unit (du, ksw(tok', page))
+    o.k = (uint32_t)(((lane >> 4) * 16 + ksw(lane & 15, page)) * 16);
+    // V: slot (d, half') holds unit (d, vsw(half', d))
+    const int d = lane >> 1;
+    o.v = (uint32_t)((d * 2 + vsw(lane & 1, d)) * 16);
+    return o;
+}
+
+// Block id of this wave's page of `tile`, as a vector load (it is consumed
+// only after the next tile barrier, which waits for it).
+__device__ __forceinline__ int db_load_id(const int32_t *bt_row, int tile)
+{
+    return bt_row[tile * 8 + (int)(threadIdx.x >> 6)];
+}
+
+// One 1 KB chunk: global_load_lds_dwordx4 with a 64-bit SGPR base, a per-lane
+// 32-bit offset and the wave's LDS destination in M0.  The instruction's
+// immediate offset would move the LDS destination as well, so it stays 0 and
+// chunk offsets go into the base.  Written as inline assembly so that the
+// compiler's wait-count bookkeeping does not treat every later LDS read as
+// dependent on the transfer (it would wait for all LDS reads at each use);
+// the transfers are waited for explicitly (vmcnt(0) before the tile
+// barrier).  The leading s_nop covers the M0-write hazard.
+__device__ __forceinline__ void db_chunk(const char *base, uint32_t off, uint32_t lds_addr)
+{
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "{m0}"(lds_addr)
+                 : "memory");
+}
+
+template <int D>
+__device__ __forceinline__ void db_issue_page(char *buf, const AttnArgs &a, int id, int kvh, int page,
+                                              const DbOffsets &o)
+{
     using G = Geo<D>;
-    static_assert(G::PAGE % 1024 == 0, "page = whole 1 KB wave chunks");
-    constexpr int CPP = G::PAGE / 1024;            // 1 KB chunks per page
-    constexpr int CHUNKS = G::NKB * CPP;           // per K (or V) tile
-    static_assert(CHUNKS % DB_WAVES == 0, "chunks split evenly over waves");
-    const ids_t<G::NKB> blk = tile_blocks<G::NKB>(a, bt_row, tile);
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    static_assert(G::PAGE == 4096, "four 1 KB chunks per page");
+    const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+    id = (uint32_t)id < nb ? id : 0;                          // ids outside the pool read block 0
     const int64_t hoff = (int64_t)kvh * BS * D;
+    const char *ks = reinterpret_cast<const char *>(a.k_cache + (int64_t)id * a.k_block_stride + hoff);
+    const char *vs = reinterpret_cast<const char *>(a.v_cache + (int64_t)id * a.v_block_stride + hoff);
+    const uint32_t kd = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)(buf + page * G::PAGE);
+    const uint32_t vd = kd + G::NKB * G::PAGE;
 #pragma unroll
-    for (int i = 0; i < CHUNKS / DB_WAVES; ++i) {
-        const int ch = w + DB_WAVES * i;
-        const int pg = ch / CPP;
-        const int slot = (ch % CPP) * 64 + lane;   // 16-byte unit within the page
-        const int64_t b = (int64_t)blk[pg];
-        // K: slot = (du, tok'), global unit (du, ksw(tok', pg))
-        const int du = slot >> 4, tk = ksw(slot & 15, pg);
-        __builtin_amdgcn_global_load_lds(a.k_cache + b * a.k_block_stride + hoff + (du * 16 + tk) * 8,
-                                         (__attribute__((address_space(3))) void *)(buf + pg * G::PAGE + (slot - lane) * 16),
-                                         16, 0, 0);
-        // V: slot = (d, half'), global unit (d, vsw(half', d))
-        const int d = slot >> 1, hf = vsw(slot & 1, d);
-        __builtin_amdgcn_global_load_lds(a.v_cache + b * a.v_block_stride + hoff + (d * 2 + hf) * 8,
-                                         (__attribute__((address_space(3))) void *)(buf + G::NKB * G::PAGE + pg * G::PAGE +
-                                                                                    (slot - lane) * 16),
-                                         16, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+        db_chunk(ks + i * 1024, o.k, kd + i * 1024);
+        db_chunk(vs + i * 1024, o.v, vd + i * 1024);
     }
 }
 
@@ -973,6 +1014,8 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 
     extern __shared__ __attribute__((aligned(16))) char lds[];
     constexpr int NCOL = NWV * CB * 16;
     constexpr int TILE_BYTES = G::LDS;            // K + V of one tile
+    static_assert(G::NKB == NWV, "one page of each tile per wave");
+    static_assert(G::PAGE % 1024 == 0, "page = whole 1 KB wave chunks");
 
     const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
     const int per = (n + 7) / 8;
@@ -1017,19 +1060,26 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 
     for (int off = 1; off < 64; off *= 2)
         min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
 
-    db_issue_tile<D, NWV>(lds, a, bt_row, kvh, 0);
+    const int page = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const DbOffsets offs = db_offsets(page);
+    db_issue_page<D>(lds, a, __builtin_amdgcn_readfirstlane(db_load_id(bt_row, 0)), kvh, page, offs);
+    int id_next = db_load_id(bt_row, min(1, last_tile));
     for (int tile = 0; tile <= last_tile; ++tile) {
         char *cur = lds + (tile & 1) * TILE_BYTES;
-        // this thread's loads of `tile` have landed; after the barrier every
-        // wave's have, and nobody still reads the other buffer
+        // this thread's loads of `tile` (and the next block id) have landed;
+        // after the barrier every wave's have, and nobody still reads the
+        // other buffer
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if ((tile + 1) * G::T > seq_len) {
             db_mask_tail<D, NWV>(cur, seq_len, tile);
             __syncthreads();
         }
-        if (tile < last_tile)
-            db_issue_tile<D, NWV>(lds + ((tile + 1) & 1) * TILE_BYTES, a, bt_row, kvh, tile + 1);
+        if (tile < last_tile) {
+            const int id = __builtin_amdgcn_readfirstlane(id_next);
+            id_next = db_load_id(bt_row, min(tile + 2, last_tile));
+            db_issue_page<D>(lds + ((tile + 1) & 1) * TILE_BYTES, a, id, kvh, page, offs);
+        }
         if (active)
         {
             if ((tile + 1) * G::T > min_lim)

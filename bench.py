@@ -348,7 +348,7 @@ def main():
                              "us_per_call": round(p_us, 2), "us_per_step_with_cache_write": round(step_us, 2),
                              "TFLOPs": round(tf, 2), "peak_TFLOPs": BF16_PEAK_TFLOPS,
                              "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops_per_call": pre.flops,
-                             "kernel": "prefill_db_kernel<128, 2, 8>",
+                             "kernel": "prefill_pp_kernel<128, 2>",
                              "hbm_traffic_bytes": recorded_traffic("prefill_kernel<128,2>")}
         log("prefill: %.2f us/call, %.1f TFLOP/s" % (p_us, tf))
         del pre

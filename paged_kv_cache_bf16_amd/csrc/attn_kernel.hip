@@ -334,15 +334,6 @@ __device__ __forceinline__ bool row_ok(const AttnArgs &a, int b, int &q0, int &q
 
 // ---------------------------------------------------------------- joint tile step (prefill)
 
-// One tile for CB column blocks of a wave, folded into their states.  Per
-// column these are exactly the operations of the fixed schedule (the same
-// MFMA chains, softmax operations and sum tree, and fold as the split-KV
-// kernel); only independent chains of different column blocks are interleaved, each K / V fragment read from LDS
-// once for all CB blocks, and fragment reads are software-pipelined one
-// step ahead (scheduling barriers keep the compiler from hoisting every read
-// to the top, which would multiply the register footprint).  MASK is false
-// when every column of the wave sees every key of the tile; the
-// multiply-only path then gives the same values as the masked one.
 // P.V for every 16-dim block of CB column blocks, each result folded into
 // its state with fma(tile, h, ACC) (the states were rescaled by gs first
 // where needed).  The V fragments of block db+1 are read while the MFMAs of
@@ -409,24 +400,19 @@ __device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB
             st[cb].acc[G::NDB - 1][i] = __builtin_fmaf(prev[cb][i], f[cb].h, st[cb].acc[G::NDB - 1][i]);
 }
 
-template <int D, int CB, bool MASK>
-__device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&cols)[CB], int tile, float scale_log2,
-                                             State<D> (&st)[CB])
+// Phase 1 of the tile step: S^T = K . Q^T for every column block.
+template <int D, int CB>
+__device__ __forceinline__ void prefill_qk(const char *kl, const Cols<D> (&cols)[CB], f32x4 (&s)[CB][Geo<D>::NKB])
 {
     using G = Geo<D>;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, c = lane & 15;
-    const char *kl = lds;
-    const char *vl = lds + G::NKB * G::PAGE;
-
     auto kaddr = [&](int kb) -> const char * {
         const int stp = kb >> 1, e = kb & 1;
         const int page = 2 * stp + (c >> 3);
         const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
         return kl + page * G::PAGE + ksw(tok, page) * 16 + g * 256;
     };
-    // ---- S^T = K . Q^T for every column block
-    f32x4 s[CB][G::NKB];
     bf16x8 kf[G::NDS], kn[G::NDS];
     {
         const char *p0 = kaddr(0);
@@ -463,13 +449,23 @@ __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&co
         __builtin_amdgcn_sched_group_barrier(0x008, G::NDS * CB, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
+}
 
+// Phase 2: softmax statistics and BF16 P^T of the tile, the fold factors,
+// the rescale of states whose reference moved, and the (R, L) fold.
+template <int D, int CB, bool MASK>
+__device__ __forceinline__ void prefill_softmax(f32x4 (&s)[CB][Geo<D>::NKB], const Cols<D> (&cols)[CB], int tile,
+                                                float scale_log2, State<D> (&st)[CB],
+                                                bf16x8 (&pf)[CB][Geo<D>::NKS], FoldF (&f)[CB])
+{
+    using G = Geo<D>;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
     // ---- softmax statistics and P^T, each step for all column blocks.
     // The max runs over raw scores (scale_log2 > 0, so max(S) * scale_log2
     // is the max of the scaled scores); p = exp2(fma(S, scale_log2, -m)).
     const int key0 = tile * G::T;
     float mx[CB], lsum[CB];
-    bf16x8 pf[CB][G::NKS];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         float mk[G::NKB];
@@ -525,7 +521,6 @@ __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&co
         lsum[cb] = sum_xor32(sum_xor16(lsum[cb]));
 
     // ---- fold factors; one wave-uniform choice of fold sequence per tile
-    FoldF f[CB];
     bool any_up = false;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -533,9 +528,8 @@ __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&co
         any_up |= __ballot(f[cb].up) != 0;
     }
 
-    // ---- states whose reference moved are rescaled (ACC * 1 is exact, so
-    // every column of the wave may take the product); then O^T = V^T . P^T
-    // per 16-dim block, folded straight into the states
+    // ---- states whose reference moved are rescaled before P.V adds into
+    // them (ACC * 1 is exact, so every column of the wave may take the product)
     if (any_up) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
@@ -545,10 +539,30 @@ __device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&co
                 for (int i = 0; i < 4; ++i)
                     st[cb].acc[db][i] = __fmul_rn(st[cb].acc[db][i], f[cb].gs);
     }
-    prefill_pv<D, CB>(vl, pf, f, st);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
         fold_stats(st[cb].R, st[cb].L, lsum[cb], f[cb]);
+}
+
+// One tile for CB column blocks of a wave, folded into their states.  Per
+// column these are exactly the operations of the fixed schedule (the same
+// MFMA chains, softmax operations and sum tree, and fold as the split-KV
+// kernel); only independent chains of different column blocks are
+// interleaved, each K / V fragment read from LDS once for all CB blocks, and
+// fragment reads are software-pipelined one step ahead.  MASK is false when
+// every column of the wave sees every key of the tile; the multiply-only
+// path then gives the same values as the masked one.
+template <int D, int CB, bool MASK>
+__device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&cols)[CB], int tile, float scale_log2,
+                                             State<D> (&st)[CB])
+{
+    using G = Geo<D>;
+    f32x4 s[CB][G::NKB];
+    bf16x8 pf[CB][G::NKS];
+    FoldF f[CB];
+    prefill_qk<D, CB>(lds, cols, s);
+    prefill_softmax<D, CB, MASK>(s, cols, tile, scale_log2, st, pf, f);
+    prefill_pv<D, CB>(lds + G::NKB * G::PAGE, pf, f, st);
 }
 
 // ---------------------------------------------------------------- streaming prefill
@@ -913,18 +927,15 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
     }
 }
 
-// ---------------------------------------------------------------- double-buffered prefill
+// ---------------------------------------------------------------- direct K/V tile transfers
 
-// Same column/tile work as prefill_kernel, for large grids: a workgroup of 8
-// waves (256 columns) owns one CU and two K/V tile buffers in LDS.  Tile t+1
-// is fetched straight from HBM into the idle buffer (global_load_lds: lane L
-// of a wave writes 16 bytes at the wave's LDS base + 16 L, so each lane
-// loads the unit that belongs at its swizzled slot) while tile t is
-// computed; no staging registers, no wait for data between tiles.  Wave w
-// stages page w of every tile (its K page and its V page, four 1 KB chunks
-// each); the page's block id is read two tiles ahead, so the id has landed
-// before the tile is issued.  V of keys at or beyond seq_len is zeroed in
-// LDS once the tail tile has landed.
+// The large-grid prefill fetches K/V tiles straight from HBM into LDS
+// (global_load_lds: lane L of a wave writes 16 bytes at the wave's LDS base +
+// 16 L, so each lane loads the unit that belongs at its swizzled slot); no
+// staging registers.  Wave w stages page w of every tile (its K page or V
+// page, four 1 KB chunks each); the page's block id is read ahead, so it has
+// landed before the tile is issued.  V of keys at or beyond seq_len is
+// zeroed in LDS once the tail tile has landed.
 
 // Per-lane source byte offsets (inside one page) of the 16-byte units that
 // chunk 0 of page `page` holds at this lane's LDS slots; chunk i adds i KB
@@ -968,34 +979,30 @@ __device__ __forceinline__ void db_chunk(const char *base, uint32_t off, uint32_
                  : "memory");
 }
 
+// This wave's page of a K (or V) tile: block `id` of `cache`, kv head kvh,
+// copied to dst + page * PAGE in four 1 KB chunks.
 template <int D>
-__device__ __forceinline__ void db_issue_page(char *buf, const AttnArgs &a, int id, int kvh, int page,
-                                              const DbOffsets &o)
+__device__ __forceinline__ void db_issue_half(char *dst, const AttnArgs &a, const uint16_t *cache, int64_t block_stride,
+                                              int id, int kvh, int page, uint32_t off)
 {
     using G = Geo<D>;
     static_assert(G::PAGE == 4096, "four 1 KB chunks per page");
     const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
     id = (uint32_t)id < nb ? id : 0;                          // ids outside the pool read block 0
-    const int64_t hoff = (int64_t)kvh * BS * D;
-    const char *ks = reinterpret_cast<const char *>(a.k_cache + (int64_t)id * a.k_block_stride + hoff);
-    const char *vs = reinterpret_cast<const char *>(a.v_cache + (int64_t)id * a.v_block_stride + hoff);
-    const uint32_t kd = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)(buf + page * G::PAGE);
-    const uint32_t vd = kd + G::NKB * G::PAGE;
+    const char *src = reinterpret_cast<const char *>(cache + (int64_t)id * block_stride + (int64_t)kvh * BS * D);
+    const uint32_t d0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)(dst + page * G::PAGE);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        db_chunk(ks + i * 1024, o.k, kd + i * 1024);
-        db_chunk(vs + i * 1024, o.v, vd + i * 1024);
-    }
+    for (int i = 0; i < 4; ++i)
+        db_chunk(src + i * 1024, off, d0 + i * 1024);
 }
 
 // Zero V of keys >= seq_len in a staged tile (only the tile holding seq_len - 1
 // and later ones can have such keys).
 template <int D, int NWV>
-__device__ __forceinline__ void db_mask_tail(char *buf, int seq_len, int tile)
+__device__ __forceinline__ void db_mask_tail(char *vl, int seq_len, int tile)
 {
     using G = Geo<D>;
     constexpr int DB_NT = NWV * 64;
-    char *vl = buf + G::NKB * G::PAGE;
     for (int u = threadIdx.x; u < G::NKB * G::UPP; u += DB_NT) {
         const int pg = u / G::UPP, slot = u % G::UPP;
         const int valid = seq_len - (tile * G::NKB + pg) * BS;
@@ -1007,15 +1014,35 @@ __device__ __forceinline__ void db_mask_tail(char *buf, int seq_len, int tile)
     }
 }
 
-template <int D, int CB, int NWV>
-__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4))) void prefill_db_kernel(AttnArgs a)
+// ---------------------------------------------------------------- ping-pong prefill
+
+// Same column/tile work and per-column arithmetic as prefill_kernel, for
+// large grids (one workgroup of 8 waves and 256 columns per CU), with
+// the two waves of each SIMD (waves w and w+4) kept half a tile apart:
+// waves 0-3 (group A) run the softmax of tile t while waves 4-7 (group B)
+// run the MFMAs of P.V(t-1) and QK(t), then the roles swap.  The wave in its
+// MFMA half runs at raised issue priority.  Two barriers per tile separate
+// the halves.
+//   slot 1: A softmax(t)                 | B P.V(t-1), QK(t)
+//   slot 2: A P.V(t), QK(t+1)            | B softmax(t)
+// K and V tiles have two LDS buffers each.  At the start of slot 2 of
+// iteration t the waves issue K(t+2) and V(t+1) into the buffers that slot 1
+// released (K(t), V(t-1)); they are waited for before the barrier that ends
+// slot 1 of iteration t+1, one slot before their first use.  P of a wave is
+// kept in the register space of its scores (the two are never live together
+// in one wave).
+template <int D, int CB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_pp_kernel(AttnArgs a)
 {
     using G = Geo<D>;
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+    constexpr int NWV = 8;
     constexpr int NCOL = NWV * CB * 16;
-    constexpr int TILE_BYTES = G::LDS;            // K + V of one tile
+    constexpr int HALF = G::NKB * G::PAGE;        // K (or V) part of one tile
     static_assert(G::NKB == NWV, "one page of each tile per wave");
-    static_assert(G::PAGE % 1024 == 0, "page = whole 1 KB wave chunks");
+    static_assert(G::NKS <= G::NKB, "P fits in the score registers");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    char *const kbuf0 = lds, *const kbuf1 = lds + HALF;
+    char *const vbuf0 = lds + 2 * HALF, *const vbuf1 = lds + 3 * HALF;
 
     const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
     const int per = (n + 7) / 8;
@@ -1035,20 +1062,20 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 
         return;
     const int col_last = min((cg + 1) * NCOL, ncols) - 1;
     const int pos_last = seq_len - q_len + col_last / a.group;
-    const int last_tile = (a.causal ? pos_last : seq_len - 1) / G::T;
+    const int last = (a.causal ? pos_last : seq_len - 1) / G::T;
     const int32_t *bt_row = a.block_tables + (int64_t)b * a.bt_stride;
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const bool grp_b = wave >= 4;
     const int c = threadIdx.x & 15;
     Cols<D> cols[CB];
-    ColInfo ci[CB];
     State<D> st[CB];
     bool active = false;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const int col = cg * NCOL + (wave * CB + cb) * 16 + c;
-        ci[cb] = col_info(a, col, kvh, q0, q_len, seq_len);
-        load_q<D>(cols[cb], a, ci[cb]);
+        const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
+        load_q<D>(cols[cb], a, ci);
         state_init<D>(st[cb]);
         active |= (cg * NCOL + (wave * CB + cb) * 16) < ncols;
     }
@@ -1060,35 +1087,113 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 
     for (int off = 1; off < 64; off *= 2)
         min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
 
-    const int page = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const DbOffsets offs = db_offsets(page);
-    db_issue_page<D>(lds, a, __builtin_amdgcn_readfirstlane(db_load_id(bt_row, 0)), kvh, page, offs);
-    int id_next = db_load_id(bt_row, min(1, last_tile));
-    for (int tile = 0; tile <= last_tile; ++tile) {
-        char *cur = lds + (tile & 1) * TILE_BYTES;
-        // this thread's loads of `tile` (and the next block id) have landed;
-        // after the barrier every wave's have, and nobody still reads the
-        // other buffer
+    const DbOffsets offs = db_offsets(wave);
+    auto issue_k = [&](char *dst, int id) { db_issue_half<D>(dst, a, a.k_cache, a.k_block_stride, id, kvh, wave, offs.k); };
+    auto issue_v = [&](char *dst, int id) { db_issue_half<D>(dst, a, a.v_cache, a.v_block_stride, id, kvh, wave, offs.v); };
+    auto kbuf = [&](int t) { return (t & 1) ? kbuf1 : kbuf0; };
+    auto vbuf = [&](int t) { return (t & 1) ? vbuf1 : vbuf0; };
+    auto softmax = [&](int tile, f32x4 (&sc)[CB][G::NKB], bf16x8 (&pf)[CB][G::NKS], FoldF (&f)[CB]) {
+        if ((tile + 1) * G::T > min_lim)
+            prefill_softmax<D, CB, true>(sc, cols, tile, a.scale_log2, st, pf, f);
+        else
+            prefill_softmax<D, CB, false>(sc, cols, tile, a.scale_log2, st, pf, f);
+    };
+
+    // ---- prologue: K(0), V(0), K(1) staged
+    {
+        const int id0 = __builtin_amdgcn_readfirstlane(db_load_id(bt_row, 0));
+        issue_k(kbuf0, id0);
+        issue_v(vbuf0, id0);
+    }
+    int id_v = 0;                                     // block id of tile t+1 (for V(t+1))
+    if (last >= 1) {
+        id_v = __builtin_amdgcn_readfirstlane(db_load_id(bt_row, 1));
+        issue_k(kbuf1, id_v);
+    }
+    int id_next = db_load_id(bt_row, min(2, last));   // tile t+2, landed by slot 2
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // Between the two slots of iteration t (every wave): the transfers of
+    // slot 2 of t-1 have landed; the tail tile's V is masked; K(t+2), V(t+1)
+    // are issued into the buffers slot 1 released.
+    auto mid = [&](int t) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if ((tile + 1) * G::T > seq_len) {
-            db_mask_tail<D, NWV>(cur, seq_len, tile);
+        if ((t + 1) * G::T > seq_len) {
+            db_mask_tail<D, NWV>(vbuf(t), seq_len, t);
             __syncthreads();
         }
-        if (tile < last_tile) {
-            const int id = __builtin_amdgcn_readfirstlane(id_next);
-            id_next = db_load_id(bt_row, min(tile + 2, last_tile));
-            db_issue_page<D>(lds + ((tile + 1) & 1) * TILE_BYTES, a, id, kvh, page, offs);
+        const int id_k = __builtin_amdgcn_readfirstlane(id_next);
+        id_next = db_load_id(bt_row, min(t + 3, last));
+        if (t + 2 <= last)
+            issue_k(kbuf(t), id_k);
+        if (t + 1 <= last)
+            issue_v(vbuf(t + 1), id_v);
+        id_v = id_k;
+    };
+
+    // The two groups run separate loops with the same barrier sequence
+    // (the branch is wave-uniform; s_barrier counts waves, not call sites).
+    // The last iteration is peeled so that no score array is carried through
+    // a path that skips its producer (it would stay live across P.V).
+    if (!grp_b) {
+        f32x4 sc[CB][G::NKB];
+        if (active)
+            prefill_qk<D, CB>(kbuf0, cols, sc);
+        __syncthreads();
+        for (int t = 0; t < last; ++t) {
+            bf16x8 pf[CB][G::NKS];
+            FoldF f[CB];
+            if (active)
+                softmax(t, sc, pf, f);                         // slot 1
+            mid(t);
+            __builtin_amdgcn_s_setprio(1);
+            if (active) {                                      // slot 2
+                prefill_pv<D, CB>(vbuf(t), pf, f, st);
+                prefill_qk<D, CB>(kbuf(t + 1), cols, sc);
+            }
+            __builtin_amdgcn_s_setprio(0);
+            __syncthreads();
+        }
+        bf16x8 pf[CB][G::NKS];
+        FoldF f[CB];
+        if (active)
+            softmax(last, sc, pf, f);
+        mid(last);
+        if (active)
+            prefill_pv<D, CB>(vbuf(last), pf, f, st);
+        __syncthreads();
+    } else {
+        bf16x8 pf[CB][G::NKS];
+        FoldF f[CB];
+        __syncthreads();
+        {
+            f32x4 sc[CB][G::NKB];
+            if (active)
+                prefill_qk<D, CB>(kbuf0, cols, sc);            // slot 1
+            mid(0);
+            if (active)
+                softmax(0, sc, pf, f);                         // slot 2
+            __syncthreads();
+        }
+        for (int t = 1; t <= last; ++t) {
+            f32x4 sc[CB][G::NKB];
+            __builtin_amdgcn_s_setprio(1);
+            if (active) {                                      // slot 1
+                prefill_pv<D, CB>(vbuf(t - 1), pf, f, st);
+                prefill_qk<D, CB>(kbuf(t), cols, sc);
+            }
+            __builtin_amdgcn_s_setprio(0);
+            mid(t);
+            if (active)
+                softmax(t, sc, pf, f);                         // slot 2
+            __syncthreads();
         }
         if (active)
-        {
-            if ((tile + 1) * G::T > min_lim)
-                prefill_tile<D, CB, true>(cur, cols, tile, a.scale_log2, st);
-            else
-                prefill_tile<D, CB, false>(cur, cols, tile, a.scale_log2, st);
-        }
+            prefill_pv<D, CB>(vbuf(last), pf, f, st);
     }
-    // column bookkeeping is recomputed here rather than kept live in the loop
+
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const ColInfo cj = col_info(a, cg * NCOL + (wave * CB + cb) * 16 + c, kvh, q0, q_len, seq_len);
@@ -1118,10 +1223,10 @@ static hipError_t prefill_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, in
     return hipGetLastError();
 }
 
-template <int D, int CB, int NWV>
-static hipError_t prefill_db_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
+template <int D, int CB>
+static hipError_t prefill_pp_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
 {
-    constexpr int NCOL = NWV * CB * 16;
+    constexpr int NCOL = 8 * CB * 16;
     a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
     const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;
     const int64_t grid = (n + 7) / 8 * 8;
@@ -1129,10 +1234,10 @@ static hipError_t prefill_db_launch(AttnArgs a, hipStream_t s, uint64_t *blocks,
         return hipSuccess;
     if (grid > 0x7fffffff)
         return hipErrorInvalidValue;
-    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_db_kernel<D, CB, NWV>,
+    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_pp_kernel<D, CB>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * Geo<D>::LDS);
     (void)attr;
-    hipLaunchKernelGGL((prefill_db_kernel<D, CB, NWV>), dim3((unsigned)grid), dim3(NWV * 64), 2 * Geo<D>::LDS, s, a);
+    hipLaunchKernelGGL((prefill_pp_kernel<D, CB>), dim3((unsigned)grid), dim3(512), 2 * Geo<D>::LDS, s, a);
     *blocks = (uint64_t)grid;
     return hipGetLastError();
 }
@@ -1146,7 +1251,7 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
     switch (head_dim) {
     case 128:
         if (db_groups >= 256)
-            return prefill_db_launch<128, 2, 8>(a, s, blocks, mq);
+            return prefill_pp_launch<128, 2>(a, s, blocks, mq);
         return prefill_launch<128, 2>(a, s, blocks, mq);
     case 256: return prefill_launch<256, 1>(a, s, blocks, mq);
     case 512: return prefill_launch<512, 1>(a, s, blocks, mq);

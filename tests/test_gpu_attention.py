@@ -119,6 +119,47 @@ def test_decode_only_sweep_many_lengths():
     _run_and_compare(w, what="decode-sweep")
 
 
+# ------------------------------------------------------------ large grids (one workgroup per CU, Dh 128)
+
+def _large_grid_blocks(w):
+    """Workgroups the Dh-128 large-grid prefill launches (256 columns each,
+    padded to a multiple of the 8 XCDs)."""
+    G = w.num_q_heads // w.num_kv_heads
+    n = w.batch * w.num_kv_heads * (-(-int(w.max_query_len) * G // 256))
+    return -(-n // 8) * 8
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_large_grid_prefill_ragged(causal):
+    """Ragged full prefills big enough for the large-grid kernel: sampled rows
+    against the oracle, every row's decode against its prefill row."""
+    lens = [2049, 1000, 300, 1537]
+    w = wl.random_case(31 + int(causal), lens, lens, 32, 8, 128, causal=causal)
+    assert _large_grid_blocks(w) >= 256
+    g, full, _ = _run_and_compare(w, rows=sample_rows(w, 96), what="large-grid causal=%d" % causal)
+    assert kvp.kvp_get_counters()["last_grid_blocks"] == _large_grid_blocks(w)
+    d = w.decode_view()
+    g.set_queries(d.q, d.query_lens)
+    bitwise(g.run(), full[w.query_start_loc[1:] - 1], "large-grid decode vs prefill last rows")
+
+
+def test_large_grid_suffix_equals_full_rows():
+    """Suffix chunks (bottom-right causal) through the large-grid kernel give
+    the full prefill's rows bitwise."""
+    lens = [3000, 2100, 3001, 2800]
+    w = wl.random_case(41, lens, lens, 32, 8, 128)
+    g = GpuCase(w)
+    full = g.run()
+    qsl = w.query_start_loc
+    for tail in (512, 777):
+        q = np.concatenate([w.q[qsl[b + 1] - tail:qsl[b + 1]] for b in range(w.batch)])
+        g.set_queries(q, [tail] * w.batch)
+        part = g.run()
+        assert kvp.kvp_get_counters()["last_grid_blocks"] == -(-(4 * 8 * (-(-tail * 4 // 256))) // 8) * 8
+        exp = np.concatenate([full[qsl[b + 1] - tail:qsl[b + 1]] for b in range(w.batch)])
+        bitwise(part, exp, "large-grid suffix %d vs full" % tail)
+
+
 # ------------------------------------------------------------ bitwise properties
 
 def _prefill_then_decode(w):

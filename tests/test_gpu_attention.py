@@ -160,6 +160,20 @@ def test_large_grid_suffix_equals_full_rows():
         bitwise(part, exp, "large-grid suffix %d vs full" % tail)
 
 
+def test_decode_long_rows():
+    """Decode rows of 65..157 tiles match the oracle and their prefill rows
+    bitwise."""
+    lens = [8193, 16384, 20000, 129]
+    w = wl.random_case(23, lens, lens, 8, 2, 128)
+    d = w.decode_view()
+    g = GpuCase(d)
+    dec = g.run()
+    compare(dec, oracle_attention(d, oracle_pool(d)), "long decode")
+    g.set_queries(w.q, w.query_lens)
+    full = g.run()
+    bitwise(dec, full[w.query_start_loc[1:] - 1], "long decode vs prefill last rows")
+
+
 # ------------------------------------------------------------ bitwise properties
 
 def _prefill_then_decode(w):

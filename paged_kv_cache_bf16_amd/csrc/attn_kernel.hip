@@ -451,6 +451,58 @@ __device__ __forceinline__ void prefill_qk(const char *kl, const Cols<D> (&cols)
     }
 }
 
+// Phase 1 for wide heads (many 32-dim steps): the same MFMA chains (one per
+// (column block, key block), head dim ascending from zero), walked with the
+// head-dim step outermost so that only one step's K fragments (plus the
+// next step's) are live.
+template <int D, int CB>
+__device__ __forceinline__ void prefill_qk_wide(const char *kl, const Cols<D> (&cols)[CB],
+                                                f32x4 (&s)[CB][Geo<D>::NKB])
+{
+    using G = Geo<D>;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    auto kaddr = [&](int kb) -> const char * {
+        const int stp = kb >> 1, e = kb & 1;
+        const int page = 2 * stp + (c >> 3);
+        const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
+        return kl + page * G::PAGE + ksw(tok, page) * 16 + g * 256;
+    };
+    const char *base[G::NKB];
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb)
+        base[kb] = kaddr(kb);
+    bf16x8 kf[G::NKB], kn[G::NKB];
+#pragma unroll
+    for (int kb = 0; kb < G::NKB; ++kb)
+        kf[kb] = *reinterpret_cast<const bf16x8 *>(base[kb]);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < G::NKB; ++kb)
+            s[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < G::NDS; ++ds) {
+        if (ds + 1 < G::NDS) {
+#pragma unroll
+            for (int kb = 0; kb < G::NKB; ++kb)
+                kn[kb] = *reinterpret_cast<const bf16x8 *>(base[kb] + (ds + 1) * 1024);
+        }
+#pragma unroll
+        for (int kb = 0; kb < G::NKB; ++kb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                s[cb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], cols[cb].qf[ds], s[cb][kb], 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < G::NKB; ++kb)
+            kf[kb] = kn[kb];
+        if (ds + 1 < G::NDS)
+            __builtin_amdgcn_sched_group_barrier(0x100, G::NKB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, G::NKB * CB, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Phase 2: softmax statistics and BF16 P^T of the tile, the fold factors,
 // the rescale of states whose reference moved, and the (R, L) fold.
 template <int D, int CB, bool MASK>
@@ -1014,6 +1066,176 @@ __device__ __forceinline__ void db_mask_tail(char *vl, int seq_len, int tile)
     }
 }
 
+// ---------------------------------------------------------------- streaming prefill, direct loads
+
+// vmcnt(N) with the other counters left alone (gfx9 s_waitcnt encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Block ids of this wave's pages of `tile` into LDS (one dword per page,
+// lanes >= npages idle), as an LDS DMA counted by vmcnt like the tile
+// transfers, so that no compiler-inserted wait stalls on the transfers.
+__device__ __forceinline__ void id_dma(const int32_t *src, int npages, uint32_t lds_addr)
+{
+    if ((int)(threadIdx.x & 63) < npages)
+        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+                     :
+                     : "v"(src + (threadIdx.x & 63)), "{m0}"(lds_addr)
+                     : "memory");
+}
+
+// Workgroup = (column group, kv head, sequence): NWV waves x CB column
+// blocks.  One LDS buffer for the K tile and one for the V tile, each
+// refilled straight from HBM as soon as its last reader is done: K(t+1) is in
+// flight during the softmax and P.V of tile t, V(t+1) during QK and the
+// softmax of tile t+1.  The tile's 1 KB chunks are split evenly over the
+// waves; wave 0 fetches the block ids of tile t+2 (to LDS) with tile t+1's V.
+// Per column the arithmetic is exactly the tile step of the other prefill
+// kernels.
+template <int D, int CB, int NWV, int WPE>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void prefill_sb_kernel(AttnArgs a)
+{
+    using G = Geo<D>;
+    constexpr int NCOL = NWV * CB * 16;
+    constexpr int HALF = G::NKB * G::PAGE;        // K (or V) part of one tile
+    constexpr int CPP = G::PAGE / 1024;           // 1 KB chunks per page
+    constexpr int CPW = G::NKB * CPP / NWV;       // K (or V) chunks per wave per tile
+    static_assert(CPW >= 1 && (G::NKB * CPP) % NWV == 0, "whole chunks per wave");
+    static_assert(CPW + 1 < 64, "vmcnt range");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    char *const kbuf = lds;
+    char *const vbuf = lds + HALF;
+    int32_t *const ids = reinterpret_cast<int32_t *>(lds + 2 * HALF);     // [2][NKB]
+
+    const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
+    const int per = (n + 7) / 8;
+    const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (j >= n)
+        return;
+    const int cgi = j % a.col_groups;
+    const int kvh = (j / a.col_groups) % a.num_kv_heads;
+    const int b = j / (a.col_groups * a.num_kv_heads);
+    const int cg = a.col_groups - 1 - cgi;           // heaviest (latest) columns first
+
+    int q0, q_len, seq_len;
+    if (!row_ok(a, b, q0, q_len, seq_len))
+        return;
+    const int ncols = q_len * a.group;
+    if (cg * NCOL >= ncols)
+        return;
+    const int col_last = min((cg + 1) * NCOL, ncols) - 1;
+    const int pos_last = seq_len - q_len + col_last / a.group;
+    const int last = (a.causal ? pos_last : seq_len - 1) / G::T;
+    const int32_t *bt_row = a.block_tables + (int64_t)b * a.bt_stride;
+
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int c = threadIdx.x & 15;
+    Cols<D> cols[CB];
+    State<D> st[CB];
+    bool active = false;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int col = cg * NCOL + (wave * CB + cb) * 16 + c;
+        const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
+        load_q<D>(cols[cb], a, ci);
+        state_init<D>(st[cb]);
+        active |= (cg * NCOL + (wave * CB + cb) * 16) < ncols;
+    }
+    int min_lim = 0x7fffffff;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        min_lim = min(min_lim, cols[cb].lim);
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2)
+        min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
+
+    auto lds_addr = [](const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p; };
+    // this wave's chunks of `tile`: block ids (from LDS) -> K or V chunks
+    auto issue = [&](bool is_k, int tile) {
+        char *const buf = is_k ? kbuf : vbuf;
+        const uint16_t *const cache = is_k ? a.k_cache : a.v_cache;
+        const int64_t stride = is_k ? a.k_block_stride : a.v_block_stride;
+        const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int ch = wave * CPW + i;
+            const int page = ch / CPP, part = ch % CPP;
+            int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
+            id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
+            const char *src = reinterpret_cast<const char *>(cache + (int64_t)id * stride + (int64_t)kvh * BS * D);
+            const DbOffsets o = db_offsets(page);
+            db_chunk(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
+        }
+    };
+    auto fetch_ids = [&](int tile) {
+        if (wave == 0)
+            id_dma(bt_row + tile * G::NKB, G::NKB, lds_addr(ids + (tile & 1) * G::NKB));
+    };
+
+    // ---- prologue: ids of tile 0, then K(0), V(0) and the ids of tile 1
+    fetch_ids(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    issue(true, 0);
+    issue(false, 0);
+    if (last >= 1)
+        fetch_ids(1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int t = 0; t <= last; ++t) {
+        f32x4 sc[CB][G::NKB];
+        bf16x8 pf[CB][G::NKS];
+        FoldF f[CB];
+        if (active) {
+            if (G::NDS > 4)
+                prefill_qk_wide<D, CB>(kbuf, cols, sc);
+            else
+                prefill_qk<D, CB>(kbuf, cols, sc);
+        }
+        __syncthreads();                                   // K(t) read by every wave
+        if (t < last)
+            issue(true, t + 1);
+        if (active) {
+            if ((t + 1) * G::T > min_lim)
+                prefill_softmax<D, CB, true>(sc, cols, t, a.scale_log2, st, pf, f);
+            else
+                prefill_softmax<D, CB, false>(sc, cols, t, a.scale_log2, st, pf, f);
+        }
+        // V(t) (issued before K(t+1)) has landed
+        if (t < last)
+            wait_vm<CPW>();
+        else
+            wait_vm<0>();
+        __syncthreads();
+        if ((t + 1) * G::T > seq_len) {
+            db_mask_tail<D, NWV>(vbuf, seq_len, t);
+            __syncthreads();
+        }
+        if (active)
+            prefill_pv<D, CB>(vbuf, pf, f, st);
+        __syncthreads();                                   // V(t) read by every wave
+        if (t < last) {
+            if (t + 2 <= last)
+                fetch_ids(t + 2);
+            issue(false, t + 1);
+            // K(t+1) and the ids of t+2 (issued before V(t+1)) have landed
+            wait_vm<CPW>();
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const ColInfo cj = col_info(a, cg * NCOL + (wave * CB + cb) * 16 + c, kvh, q0, q_len, seq_len);
+        if (cj.lim > 0)
+            store_out<D>(a, cj, st[cb]);
+    }
+}
+
 // ---------------------------------------------------------------- ping-pong prefill
 
 // Same column/tile work and per-column arithmetic as prefill_kernel, for
@@ -1223,6 +1445,26 @@ static hipError_t prefill_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, in
     return hipGetLastError();
 }
 
+template <int D, int CB, int NWV, int WPE>
+static hipError_t prefill_sb_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
+{
+    constexpr int NCOL = NWV * CB * 16;
+    constexpr int LDS_BYTES = Geo<D>::LDS + 2 * Geo<D>::NKB * 4;
+    a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
+    const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;
+    const int64_t grid = (n + 7) / 8 * 8;
+    if (grid <= 0)
+        return hipSuccess;
+    if (grid > 0x7fffffff)
+        return hipErrorInvalidValue;
+    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_sb_kernel<D, CB, NWV, WPE>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    (void)attr;
+    hipLaunchKernelGGL((prefill_sb_kernel<D, CB, NWV, WPE>), dim3((unsigned)grid), dim3(NWV * 64), LDS_BYTES, s, a);
+    *blocks = (uint64_t)grid;
+    return hipGetLastError();
+}
+
 template <int D, int CB>
 static hipError_t prefill_pp_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
 {
@@ -1252,9 +1494,11 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
     case 128:
         if (db_groups >= 256)
             return prefill_pp_launch<128, 2>(a, s, blocks, mq);
-        return prefill_launch<128, 2>(a, s, blocks, mq);
-    case 256: return prefill_launch<256, 1>(a, s, blocks, mq);
-    case 512: return prefill_launch<512, 1>(a, s, blocks, mq);
+        if ((int64_t)a.num_seqs * a.num_kv_heads * ((mq * a.group + 127) / 128) >= 256)
+            return prefill_sb_launch<128, 2, 4, 2>(a, s, blocks, mq);
+        return prefill_sb_launch<128, 1, 4, 2>(a, s, blocks, mq);
+    case 256: return prefill_sb_launch<256, 1, 8, 2>(a, s, blocks, mq);
+    case 512: return prefill_sb_launch<512, 1, 8, 2>(a, s, blocks, mq);
     default: return hipErrorInvalidValue;
     }
 }

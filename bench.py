@@ -349,7 +349,7 @@ def main():
                              "TFLOPs": round(tf, 2), "peak_TFLOPs": BF16_PEAK_TFLOPS,
                              "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops_per_call": pre.flops,
                              "kernel": "prefill_pp_kernel<128, 2>",
-                             "hbm_traffic_bytes": recorded_traffic("prefill_kernel<128,2>")}
+                             "hbm_traffic_bytes": recorded_traffic("prefill_pp_kernel<128,2>")}
         log("prefill: %.2f us/call, %.1f TFLOP/s" % (p_us, tf))
         del pre
 

@@ -170,6 +170,12 @@ int kvp_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
  * Query head h reads kv head h / (num_q_heads / num_kv_heads).
  * Rows with q_len == 0 are skipped; rows that violate 0 <= q_len <=
  * seq_len <= max_seq_len produce no output and no memory access.
+ *   workspace        device, kvp_workspace_bytes(pool, num_q_heads, num_seqs,
+ *                    max_seq_len) bytes, 16-byte aligned.  Required when
+ *                    max_query_len * G <= 16 (decode).  Otherwise optional:
+ *                    given (large enough) with num_seqs > 1, rows whose
+ *                    q_len * G <= 16 take the split-KV decode path and the
+ *                    others the prefill path, in two launches on `stream`.
  * Numerics: one fixed arithmetic schedule (KV tiles and their softmax folds
  * at fixed absolute positions), so an output row's bits do not depend on
  * the batch, the other rows, the query count or the kernel chosen: a decode

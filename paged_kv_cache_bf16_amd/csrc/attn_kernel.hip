@@ -12,20 +12,23 @@
 //     head_dim 128, 64 otherwise).  For one query column and one tile:
 //       S = K . q with BF16 MFMA (v_mfma_f32_16x16x32_bf16), FP32 accumulate,
 //           the head dimension walked in 32-wide steps in ascending order;
-//       t = S * (scale*log2 e), -inf for keys the column does not see;
-//       m = max t;  p = exp2(t - m) (v_exp_f32);  l = sum p in a fixed tree;
+//       S = -inf for keys the column does not see;
+//       m = max(S) * c with c = scale * log2 e (c > 0, so the max of the
+//           scaled scores);  p = exp2(fma(S, c, -m)) (v_exp_f32);
+//       l = sum p in a fixed tree;
 //       acc = P . V with P = bf16(p), MFMA over the tile's keys in 32-key
 //           steps in ascending order.
-//   * Tiles are folded into the running (M, L, ACC) in ascending order:
-//       if m > M:  f = exp2(M - m);  ACC = fma(ACC, f, acc); L = fma(L, f, l); M = m
-//       else:      f = exp2(m - M);  ACC = fma(acc, f, ACC); L = fma(l, f, L)
-//     starting from M = -inf, L = 0, ACC = 0 (a tile a column cannot see is a
-//     no-op).  The output is bf16(ACC * (1 / L) + 0).
+//   * Tiles are folded into the running (R, L, ACC) in ascending order, from
+//     (-inf, 0, 0); R is the running max rounded up to a multiple of 16:
+//       R' = max(R, ref(m));  gs = R' > R ? exp2(R - R') : 1;
+//       h = exp2(m - R') (0 for an empty tile);
+//       ACC = fma(acc, h, ACC * gs);  L = fma(l, h, L * gs);  R = R'.
+//     The output is bf16(ACC * (1 / L) + 0).
 //   * No implicit FMA contraction (the library is built -ffp-contract=off);
 //     every FMA above is written explicitly.
 // Who computes a tile (a streaming prefill workgroup, or one split-KV
-// workgroup per tile whose partial the last-arriving workgroup folds) never
-// changes these operations, so decode and prefill rows agree bit for bit.
+// workgroup per tile whose partial a fold kernel combines) never changes
+// these operations, so decode and prefill rows agree bit for bit.
 //
 // MFMA operand plumbing.  With S^T = K . Q^T the score tile comes out with
 // the keys along the accumulator's row axis and query columns along lanes,
@@ -36,10 +39,10 @@
 // dim-major in its pages ([d][16 tokens]), so those eight keys of one dim
 // are one 16-byte LDS read.
 //
-// LDS: the K and V pages of the current tile are staged (one kv head), with
-// a 16-byte-unit XOR swizzle that keeps the MFMA operand reads free of bank
-// conflicts.  Keys at or beyond seq_len read as zero (K and V) so padded or
-// poisoned page tails never reach the arithmetic.
+// LDS: the K and V pages of a tile are staged (one kv head), with a
+// 16-byte-unit XOR swizzle that keeps the MFMA operand reads free of bank
+// conflicts.  V of keys at or beyond seq_len is zeroed and their scores are
+// -inf, so padded or poisoned page tails never reach the arithmetic.
 #include "kvp_internal.h"
 
 namespace kvp {
@@ -140,52 +143,6 @@ __device__ __forceinline__ u32x4 mask_tokens(u32x4 v, int tok0, int valid)
         v[j] &= (lo | hi);
     }
     return v;
-}
-
-// Copies the K and V pages of tile `tile` (kv head kvh) into LDS.  V of keys
-// at or beyond seq_len is zero; K of those keys is left as read (its scores
-// are masked).  All loads are issued before any is consumed.
-template <int D>
-__device__ __forceinline__ void stage_tile(char *lds, const AttnArgs &a, const int32_t *bt_row,
-                                           int seq_len, int kvh, int tile)
-{
-    using G = Geo<D>;
-    constexpr int IT = G::NKB * G::UPP / NT;
-    char *kl = lds;
-    char *vl = lds + G::NKB * G::PAGE;
-    const int tid = threadIdx.x;
-    const ids_t<G::NKB> blk = tile_blocks<G::NKB>(a, bt_row, tile);
-    const int64_t hoff = (int64_t)kvh * BS * D;
-    u32x4 kv[IT], vv[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int u = tid + it * NT;
-        const int p = u / G::UPP;           // compile-time per iteration (UPP % NT == 0)
-        const int w = u % G::UPP;
-        kv[it] = *reinterpret_cast<const u32x4 *>(a.k_cache + (int64_t)blk[p] * a.k_block_stride + hoff + (int64_t)w * 8);
-        vv[it] = *reinterpret_cast<const u32x4 *>(a.v_cache + (int64_t)blk[p] * a.v_block_stride + hoff + (int64_t)w * 8);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if ((tile + 1) * G::T > seq_len) {
-        // the tile reaches past seq_len: zero V of the keys beyond it
-#pragma unroll
-        for (int it = 0; it < IT; ++it) {
-            const int u = tid + it * NT;
-            const int p = u / G::UPP;
-            const int w = u % G::UPP;
-            vv[it] = mask_tokens(vv[it], (w & 1) * 8, seq_len - (tile * G::NKB + p) * BS);
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int u = tid + it * NT;
-        const int p = u / G::UPP;
-        const int w = u % G::UPP;
-        const int du = w >> 4, tok = w & 15;
-        *reinterpret_cast<u32x4 *>(kl + p * G::PAGE + (du * 16 + ksw(tok, p)) * 16) = kv[it];
-        const int d = w >> 1, half = w & 1;
-        *reinterpret_cast<u32x4 *>(vl + p * G::PAGE + (d * 2 + vsw(half, d)) * 16) = vv[it];
-    }
 }
 
 // ---------------------------------------------------------------- tile step
@@ -596,105 +553,84 @@ __device__ __forceinline__ void prefill_softmax(f32x4 (&s)[CB][Geo<D>::NKB], con
         fold_stats(st[cb].R, st[cb].L, lsum[cb], f[cb]);
 }
 
-// One tile for CB column blocks of a wave, folded into their states.  Per
-// column these are exactly the operations of the fixed schedule (the same
-// MFMA chains, softmax operations and sum tree, and fold as the split-KV
-// kernel); only independent chains of different column blocks are
-// interleaved, each K / V fragment read from LDS once for all CB blocks, and
-// fragment reads are software-pipelined one step ahead.  MASK is false when
-// every column of the wave sees every key of the tile; the multiply-only
-// path then gives the same values as the masked one.
-template <int D, int CB, bool MASK>
-__device__ __forceinline__ void prefill_tile(const char *lds, const Cols<D> (&cols)[CB], int tile, float scale_log2,
-                                             State<D> (&st)[CB])
+// P.V with DG 16-dim blocks in flight at once (independent MFMA chains for
+// waves that have their SIMD to themselves): per block the same chain (32-key
+// steps ascending from zero) and the same fold fma(tile, h, ACC) as
+// prefill_pv.
+template <int D, int CB, int DG>
+__device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS],
+                                               const FoldF (&f)[CB], State<D> (&st)[CB])
 {
     using G = Geo<D>;
-    f32x4 s[CB][G::NKB];
-    bf16x8 pf[CB][G::NKS];
-    FoldF f[CB];
-    prefill_qk<D, CB>(lds, cols, s);
-    prefill_softmax<D, CB, MASK>(s, cols, tile, scale_log2, st, pf, f);
-    prefill_pv<D, CB>(lds + G::NKB * G::PAGE, pf, f, st);
+    static_assert(G::NDB % DG == 0, "whole groups");
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    auto vaddr = [&](int db, int stp) -> const char * {
+        const int d = 16 * db + c;
+        return vl + (g >> 1) * G::PAGE + (d * 2 + vsw(g & 1, d)) * 16 + 2 * stp * G::PAGE;
+    };
+#pragma unroll
+    for (int db0 = 0; db0 < G::NDB; db0 += DG) {
+        f32x4 o[CB][DG];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int d = 0; d < DG; ++d)
+                o[cb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 vf[DG], vn[DG];
+#pragma unroll
+        for (int d = 0; d < DG; ++d)
+            vf[d] = *reinterpret_cast<const bf16x8 *>(vaddr(db0 + d, 0));
+#pragma unroll
+        for (int stp = 0; stp < G::NKS; ++stp) {
+            if (stp + 1 < G::NKS) {
+#pragma unroll
+                for (int d = 0; d < DG; ++d)
+                    vn[d] = *reinterpret_cast<const bf16x8 *>(vaddr(db0 + d, stp + 1));
+            }
+#pragma unroll
+            for (int d = 0; d < DG; ++d)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    o[cb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], pf[cb][stp], o[cb][d], 0, 0, 0);
+#pragma unroll
+            for (int d = 0; d < DG; ++d)
+                vf[d] = vn[d];
+            if (stp + 1 < G::NKS)
+                __builtin_amdgcn_sched_group_barrier(0x100, DG, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, DG * CB, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int d = 0; d < DG; ++d)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st[cb].acc[db0 + d][i] = __builtin_fmaf(o[cb][d][i], f[cb].h, st[cb].acc[db0 + d][i]);
+    }
 }
 
-// ---------------------------------------------------------------- streaming prefill
-
-// Workgroup = (column group, kv head, sequence); 4 waves x CB column blocks.
-// Walks the tiles in ascending order, folding each into registers.
+// The tile step's QK and P.V for a wave: single-column-block waves (which
+// often have their SIMD to themselves) take the variants with several
+// independent MFMA chains in flight.
 template <int D, int CB>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 512 ? 1 : 2, 2))) void prefill_kernel(AttnArgs a)
+__device__ __forceinline__ void tile_qk(const char *kl, const Cols<D> (&cols)[CB], f32x4 (&s)[CB][Geo<D>::NKB])
 {
-    using G = Geo<D>;
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    constexpr int NCOL = NW * CB * 16;
+    if (CB == 1 || Geo<D>::NDS > 4)
+        prefill_qk_wide<D, CB>(kl, cols, s);
+    else
+        prefill_qk<D, CB>(kl, cols, s);
+}
 
-    // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a
-    // contiguous run of work items so one kv head's pages stay in its L2.
-    const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
-    const int per = (n + 7) / 8;
-    const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (j >= n)
-        return;
-    const int cgi = j % a.col_groups;
-    const int kvh = (j / a.col_groups) % a.num_kv_heads;
-    const int b = j / (a.col_groups * a.num_kv_heads);
-    const int cg = a.col_groups - 1 - cgi;           // heaviest (latest) columns first
-
-    int q0, q_len, seq_len;
-    if (!row_ok(a, b, q0, q_len, seq_len))
-        return;
-    const int ncols = q_len * a.group;
-    if (cg * NCOL >= ncols)
-        return;
-    const int col_last = min((cg + 1) * NCOL, ncols) - 1;
-    const int pos_last = seq_len - q_len + col_last / a.group;
-    const int last_tile = (a.causal ? pos_last : seq_len - 1) / G::T;
-    const int32_t *bt_row = a.block_tables + (int64_t)b * a.bt_stride;
-
-    const int wave = threadIdx.x >> 6;
-    const int c = threadIdx.x & 15;
-    Cols<D> cols[CB];
-    ColInfo ci[CB];
-    State<D> st[CB];
-    bool active = false;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        const int col = cg * NCOL + (wave * CB + cb) * 16 + c;
-        ci[cb] = col_info(a, col, kvh, q0, q_len, seq_len);
-        load_q<D>(cols[cb], a, ci[cb]);
-        state_init<D>(st[cb]);
-        active |= (cg * NCOL + (wave * CB + cb) * 16) < ncols;
-    }
-
-    // smallest key limit of the wave's columns: tiles ending at or below it
-    // need no mask
-    int min_lim = 0x7fffffff;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-        min_lim = min(min_lim, cols[cb].lim);
-#pragma unroll
-    for (int off = 1; off < 64; off *= 2)
-        min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
-
-    for (int tile = 0; tile <= last_tile; ++tile) {
-        __syncthreads();
-        stage_tile<D>(lds, a, bt_row, seq_len, kvh, tile);
-        __syncthreads();
-        if (active)
-        {
-            if ((tile + 1) * G::T > min_lim)
-                prefill_tile<D, CB, true>(lds, cols, tile, a.scale_log2, st);
-            else
-                prefill_tile<D, CB, false>(lds, cols, tile, a.scale_log2, st);
-        }
-    }
-    // column bookkeeping is recomputed here rather than kept live in the loop
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        const ColInfo cj = col_info(a, cg * NCOL + (wave * CB + cb) * 16 + c, kvh, q0, q_len, seq_len);
-        if (cj.lim > 0)
-            store_out<D>(a, cj, st[cb]);
-    }
+template <int D, int CB>
+__device__ __forceinline__ void tile_pv(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS], const FoldF (&f)[CB],
+                                        State<D> (&st)[CB])
+{
+    if (CB == 1)
+        prefill_pv_grp<D, CB, (D == 128 ? 8 : 4)>(vl, pf, f, st);
+    else
+        prefill_pv<D, CB>(vl, pf, f, st);
 }
 
 // ---------------------------------------------------------------- split-KV (decode)
@@ -1125,7 +1061,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     if (!row_ok(a, b, q0, q_len, seq_len))
         return;
     const int ncols = q_len * a.group;
-    if (cg * NCOL >= ncols)
+    if (cg * NCOL >= ncols || ncols <= a.split_cols)
         return;
     const int col_last = min((cg + 1) * NCOL, ncols) - 1;
     const int pos_last = seq_len - q_len + col_last / a.group;
@@ -1192,10 +1128,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
         bf16x8 pf[CB][G::NKS];
         FoldF f[CB];
         if (active) {
-            if (G::NDS > 4)
-                prefill_qk_wide<D, CB>(kbuf, cols, sc);
-            else
-                prefill_qk<D, CB>(kbuf, cols, sc);
+            tile_qk<D, CB>(kbuf, cols, sc);
         }
         __syncthreads();                                   // K(t) read by every wave
         if (t < last)
@@ -1217,7 +1150,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             __syncthreads();
         }
         if (active)
-            prefill_pv<D, CB>(vbuf, pf, f, st);
+            tile_pv<D, CB>(vbuf, pf, f, st);
         __syncthreads();                                   // V(t) read by every wave
         if (t < last) {
             if (t + 2 <= last)
@@ -1236,9 +1169,137 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     }
 }
 
+// Double-buffered variant for workgroups that own a CU: two K+V tile
+// buffers; tile t+1 (and the block ids of t+2) are fetched while tile t is
+// computed, one barrier per tile.  Same chunk split and per-column arithmetic
+// as prefill_sb_kernel.
+template <int D, int CB, int NWV, int WPE>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void prefill_db_kernel(AttnArgs a)
+{
+    using G = Geo<D>;
+    constexpr int NCOL = NWV * CB * 16;
+    constexpr int HALF = G::NKB * G::PAGE;        // K (or V) part of one tile
+    constexpr int CPP = G::PAGE / 1024;           // 1 KB chunks per page
+    constexpr int CPW = G::NKB * CPP / NWV;       // K (or V) chunks per wave per tile
+    static_assert(CPW >= 1 && (G::NKB * CPP) % NWV == 0, "whole chunks per wave");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    int32_t *const ids = reinterpret_cast<int32_t *>(lds + 4 * HALF);     // [2][NKB]
+
+    const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
+    const int per = (n + 7) / 8;
+    const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (j >= n)
+        return;
+    const int cgi = j % a.col_groups;
+    const int kvh = (j / a.col_groups) % a.num_kv_heads;
+    const int b = j / (a.col_groups * a.num_kv_heads);
+    const int cg = a.col_groups - 1 - cgi;           // heaviest (latest) columns first
+
+    int q0, q_len, seq_len;
+    if (!row_ok(a, b, q0, q_len, seq_len))
+        return;
+    const int ncols = q_len * a.group;
+    if (cg * NCOL >= ncols || ncols <= a.split_cols)
+        return;
+    const int col_last = min((cg + 1) * NCOL, ncols) - 1;
+    const int pos_last = seq_len - q_len + col_last / a.group;
+    const int last = (a.causal ? pos_last : seq_len - 1) / G::T;
+    const int32_t *bt_row = a.block_tables + (int64_t)b * a.bt_stride;
+
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int c = threadIdx.x & 15;
+    Cols<D> cols[CB];
+    State<D> st[CB];
+    bool active = false;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int col = cg * NCOL + (wave * CB + cb) * 16 + c;
+        const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
+        load_q<D>(cols[cb], a, ci);
+        state_init<D>(st[cb]);
+        active |= (cg * NCOL + (wave * CB + cb) * 16) < ncols;
+    }
+    int min_lim = 0x7fffffff;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        min_lim = min(min_lim, cols[cb].lim);
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2)
+        min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
+
+    auto lds_addr = [](const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p; };
+    auto kbuf = [&](int tile) { return lds + (tile & 1) * 2 * HALF; };
+    // this wave's chunks of `tile` (K and V): block ids (from LDS) -> chunks
+    auto issue = [&](int tile) {
+        char *const buf = kbuf(tile);
+        const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int ch = wave * CPW + i;
+            const int page = ch / CPP, part = ch % CPP;
+            int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
+            id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
+            const int64_t hoff = (int64_t)kvh * BS * D;
+            const char *ks = reinterpret_cast<const char *>(a.k_cache + (int64_t)id * a.k_block_stride + hoff);
+            const char *vs = reinterpret_cast<const char *>(a.v_cache + (int64_t)id * a.v_block_stride + hoff);
+            const DbOffsets o = db_offsets(page);
+            db_chunk(ks + part * 1024, o.k, lds_addr(buf + page * G::PAGE + part * 1024));
+            db_chunk(vs + part * 1024, o.v, lds_addr(buf + HALF + page * G::PAGE + part * 1024));
+        }
+    };
+    auto fetch_ids = [&](int tile) {
+        if (wave == 0)
+            id_dma(bt_row + tile * G::NKB, G::NKB, lds_addr(ids + (tile & 1) * G::NKB));
+    };
+
+    // ---- prologue: ids of tile 0, tile 0, ids of tile 1
+    fetch_ids(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    issue(0);
+    if (last >= 1)
+        fetch_ids(1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int t = 0; t <= last; ++t) {
+        // tile t+1 and the ids of t+2 go out while tile t is computed; the
+        // buffers they fill were last read in iteration t-1
+        if (t < last) {
+            issue(t + 1);
+            if (t + 2 <= last)
+                fetch_ids(t + 2);
+        }
+        char *const cur = kbuf(t);
+        if ((t + 1) * G::T > seq_len) {
+            db_mask_tail<D, NWV>(cur + HALF, seq_len, t);
+            __syncthreads();
+        }
+        if (active) {
+            f32x4 sc[CB][G::NKB];
+            bf16x8 pf[CB][G::NKS];
+            FoldF f[CB];
+            tile_qk<D, CB>(cur, cols, sc);
+            if ((t + 1) * G::T > min_lim)
+                prefill_softmax<D, CB, true>(sc, cols, t, a.scale_log2, st, pf, f);
+            else
+                prefill_softmax<D, CB, false>(sc, cols, t, a.scale_log2, st, pf, f);
+            tile_pv<D, CB>(cur + HALF, pf, f, st);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const ColInfo cj = col_info(a, cg * NCOL + (wave * CB + cb) * 16 + c, kvh, q0, q_len, seq_len);
+        if (cj.lim > 0)
+            store_out<D>(a, cj, st[cb]);
+    }
+}
+
 // ---------------------------------------------------------------- ping-pong prefill
 
-// Same column/tile work and per-column arithmetic as prefill_kernel, for
+// Same column/tile work and per-column arithmetic as prefill_db_kernel, for
 // large grids (one workgroup of 8 waves and 256 columns per CU), with
 // the two waves of each SIMD (waves w and w+4) kept half a tile apart:
 // waves 0-3 (group A) run the softmax of tile t while waves 4-7 (group B)
@@ -1280,7 +1341,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (!row_ok(a, b, q0, q_len, seq_len))
         return;
     const int ncols = q_len * a.group;
-    if (cg * NCOL >= ncols)
+    if (cg * NCOL >= ncols || ncols <= a.split_cols)
         return;
     const int col_last = min((cg + 1) * NCOL, ncols) - 1;
     const int pos_last = seq_len - q_len + col_last / a.group;
@@ -1426,25 +1487,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-template <int D, int CB>
-static hipError_t prefill_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
-{
-    constexpr int NCOL = NW * CB * 16;
-    a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
-    const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;
-    const int64_t grid = (n + 7) / 8 * 8;
-    if (grid <= 0)
-        return hipSuccess;
-    if (grid > 0x7fffffff)
-        return hipErrorInvalidValue;
-    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_kernel<D, CB>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, Geo<D>::LDS);
-    (void)attr;
-    hipLaunchKernelGGL((prefill_kernel<D, CB>), dim3((unsigned)grid), dim3(NT), Geo<D>::LDS, s, a);
-    *blocks = (uint64_t)grid;
-    return hipGetLastError();
-}
-
 template <int D, int CB, int NWV, int WPE>
 static hipError_t prefill_sb_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
 {
@@ -1461,6 +1503,26 @@ static hipError_t prefill_sb_launch(AttnArgs a, hipStream_t s, uint64_t *blocks,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     (void)attr;
     hipLaunchKernelGGL((prefill_sb_kernel<D, CB, NWV, WPE>), dim3((unsigned)grid), dim3(NWV * 64), LDS_BYTES, s, a);
+    *blocks = (uint64_t)grid;
+    return hipGetLastError();
+}
+
+template <int D, int CB, int NWV, int WPE>
+static hipError_t prefill_db_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
+{
+    constexpr int NCOL = NWV * CB * 16;
+    constexpr int LDS_BYTES = 2 * Geo<D>::LDS + 2 * Geo<D>::NKB * 4;
+    a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
+    const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;
+    const int64_t grid = (n + 7) / 8 * 8;
+    if (grid <= 0)
+        return hipSuccess;
+    if (grid > 0x7fffffff)
+        return hipErrorInvalidValue;
+    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_db_kernel<D, CB, NWV, WPE>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    (void)attr;
+    hipLaunchKernelGGL((prefill_db_kernel<D, CB, NWV, WPE>), dim3((unsigned)grid), dim3(NWV * 64), LDS_BYTES, s, a);
     *blocks = (uint64_t)grid;
     return hipGetLastError();
 }
@@ -1487,17 +1549,17 @@ static hipError_t prefill_pp_launch(AttnArgs a, hipStream_t s, uint64_t *blocks,
 hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks)
 {
     const int mq = max_query_len;
-    // Double-buffered 8-wave kernel when it still yields a workgroup per CU
-    // (256 CUs); the 4-wave kernel keeps small grids spread over the chip.
+    // Dh 128: the ping-pong kernel (256 columns per workgroup) when it still
+    // yields a workgroup per CU (256 CUs), else the double-buffered kernel
+    // with 128 columns.  Dh 256: double-buffered.  Dh 512: one K and one V
+    // buffer (a double-buffered tile would not fit in LDS).
     const int64_t db_groups = (int64_t)a.num_seqs * a.num_kv_heads * ((mq * a.group + 255) / 256);
     switch (head_dim) {
     case 128:
         if (db_groups >= 256)
             return prefill_pp_launch<128, 2>(a, s, blocks, mq);
-        if ((int64_t)a.num_seqs * a.num_kv_heads * ((mq * a.group + 127) / 128) >= 256)
-            return prefill_sb_launch<128, 2, 4, 2>(a, s, blocks, mq);
-        return prefill_sb_launch<128, 1, 4, 2>(a, s, blocks, mq);
-    case 256: return prefill_sb_launch<256, 1, 8, 2>(a, s, blocks, mq);
+        return prefill_db_launch<128, 1, 8, 2>(a, s, blocks, mq);
+    case 256: return prefill_db_launch<256, 1, 8, 2>(a, s, blocks, mq);
     case 512: return prefill_sb_launch<512, 1, 8, 2>(a, s, blocks, mq);
     default: return hipErrorInvalidValue;
     }

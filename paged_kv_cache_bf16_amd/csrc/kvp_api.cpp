@@ -295,17 +295,27 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
     a.scale_log2 = scale * 1.44269504088896340736f;
     a.causal = causal;
     a.ws_acc = a.ws_m = a.ws_l = nullptr;
+    a.split_cols = 0;
 
-    const bool split = (int64_t)max_query_len * G <= kvp::kSplitCols;
+    // Rows with q_len * G <= 16 (decode, short suffixes) take the split-KV
+    // path, which spreads their KV tiles over the chip; the rest stream
+    // through a prefill kernel.  A call with only such rows needs the
+    // workspace; a mixed batch of several rows uses both paths when a large
+    // enough workspace is given (both paths give the same bits per row).
+    const bool split_only = (int64_t)max_query_len * G <= kvp::kSplitCols;
     if (num_seqs > 65535 || d.num_kv_heads > 65535)
         return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_seqs and num_kv_heads must be <= 65535");
-    if (split) {
-        const kvp::Workspace w = kvp::workspace_layout(num_seqs, d.num_kv_heads, a.max_tiles, D);
+    const kvp::Workspace w = kvp::workspace_layout(num_seqs, d.num_kv_heads, a.max_tiles, D);
+    const bool ws_ok = workspace && aligned16(workspace) && workspace_bytes >= w.total;
+    if (split_only) {
         if (!workspace || !aligned16(workspace))
             return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: decode needs a 16-byte aligned workspace");
         if (workspace_bytes < w.total)
             return fail(KVP_ERR_WORKSPACE_TOO_SMALL, "paged_attention: workspace %zu < %zu bytes", workspace_bytes,
                         w.total);
+    }
+    const bool use_split = split_only || (num_seqs > 1 && ws_ok);
+    if (use_split) {
         char *base = (char *)workspace;
         a.ws_acc = (float *)(base + w.acc_off);
         a.ws_m = (float *)(base + w.m_off);
@@ -316,7 +326,9 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
             return hip_fail(e, "paged_attention split-KV launch");
         g_split_launches++;
         g_last_grid = blocks;
-    } else {
+        a.split_cols = kvp::kSplitCols;
+    }
+    if (!split_only) {
         uint64_t blocks = 0;
         hipError_t e = kvp::launch_prefill(a, D, max_query_len, (hipStream_t)stream, &blocks);
         if (e != hipSuccess)

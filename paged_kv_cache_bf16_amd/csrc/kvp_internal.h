@@ -43,6 +43,7 @@ struct AttnArgs {
     int32_t max_seq_len, max_tiles, col_groups;
     float scale_log2;          // softmax scale * log2(e), rounded once on the host
     int32_t causal;
+    int32_t split_cols;        // prefill kernels skip rows with q_len * G <= split_cols
     // split-KV workspace
     float *ws_acc;             // [B][Hkv][max_tiles][kSplitCols][D]
     float *ws_m, *ws_l;        // [B][Hkv][max_tiles][kSplitCols]

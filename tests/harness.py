@@ -60,7 +60,7 @@ class GpuCase:
         self.q = dev_bits(q_bits)
         self.out = torch.zeros_like(self.q)
 
-    def run(self, causal=None, max_seq_len=None):
+    def run(self, causal=None, max_seq_len=None, use_workspace=True):
         """Run paged_attention; max_seq_len overrides the host bound (it must
         cover every row; a larger bound can select a different kernel path)."""
         w = self.w
@@ -68,7 +68,8 @@ class GpuCase:
         ms = int(self.seq_lens_h.max(initial=0)) if max_seq_len is None else int(max_seq_len)
         kvp.paged_attention(self.pool, self.q, self.out, w.num_q_heads, self.bt, self.seq_lens, self.qsl,
                             int(self.qlens_h.max(initial=0)), ms, w.scale,
-                            w.causal if causal is None else causal, workspace=self.ws)
+                            w.causal if causal is None else causal,
+                            workspace=self.ws if use_workspace else None)
         torch.cuda.synchronize()
         return host_bits(self.out)
 

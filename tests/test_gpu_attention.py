@@ -160,6 +160,21 @@ def test_large_grid_suffix_equals_full_rows():
         bitwise(part, exp, "large-grid suffix %d vs full" % tail)
 
 
+def test_mixed_batch_split_and_prefill_paths_agree():
+    """With a workspace, rows of a mixed batch whose q_len * G <= 16 take the
+    split-KV path and the others a prefill kernel; without one, every row
+    streams through the prefill kernel.  Both give the same bits."""
+    w = wl.random_case(29, [300, 2000, 129, 700, 4100], [300, 1, 4, 33, 2], 8, 2, 128)
+    g = GpuCase(w)
+    before = kvp.kvp_get_counters()["split_kv_launches"]
+    both = g.run()
+    assert kvp.kvp_get_counters()["split_kv_launches"] == before + 1
+    alone = g.run(use_workspace=False)
+    assert kvp.kvp_get_counters()["split_kv_launches"] == before + 1
+    bitwise(both, alone, "mixed batch: split + prefill vs prefill only")
+    compare(both, oracle_attention(w, oracle_pool(w)), "mixed batch")
+
+
 def test_decode_long_rows():
     """Decode rows of 65..157 tiles match the oracle and their prefill rows
     bitwise."""

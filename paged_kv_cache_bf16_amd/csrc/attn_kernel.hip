@@ -460,12 +460,13 @@ __device__ __forceinline__ void prefill_qk_wide(const char *kl, const Cols<D> (&
     }
 }
 
-// Phase 2: softmax statistics and BF16 P^T of the tile, the fold factors,
-// the rescale of states whose reference moved, and the (R, L) fold.
+// Phase 2: softmax statistics and BF16 P^T of the tile, the fold factors
+// and the (R, L) fold; returns whether some column's reference moved (its
+// ACC must then be rescaled by gs before this tile's P.V is added).
 template <int D, int CB, bool MASK>
-__device__ __forceinline__ void prefill_softmax(f32x4 (&s)[CB][Geo<D>::NKB], const Cols<D> (&cols)[CB], int tile,
-                                                float scale_log2, State<D> (&st)[CB],
-                                                bf16x8 (&pf)[CB][Geo<D>::NKS], FoldF (&f)[CB])
+__device__ __forceinline__ bool prefill_softmax_stats(f32x4 (&s)[CB][Geo<D>::NKB], const Cols<D> (&cols)[CB],
+                                                      int tile, float scale_log2, State<D> (&st)[CB],
+                                                      bf16x8 (&pf)[CB][Geo<D>::NKS], FoldF (&f)[CB])
 {
     using G = Geo<D>;
     const int lane = threadIdx.x & 63;
@@ -537,20 +538,33 @@ __device__ __forceinline__ void prefill_softmax(f32x4 (&s)[CB][Geo<D>::NKB], con
         any_up |= __ballot(f[cb].up) != 0;
     }
 
-    // ---- states whose reference moved are rescaled before P.V adds into
-    // them (ACC * 1 is exact, so every column of the wave may take the product)
-    if (any_up) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int db = 0; db < G::NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    st[cb].acc[db][i] = __fmul_rn(st[cb].acc[db][i], f[cb].gs);
-    }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
         fold_stats(st[cb].R, st[cb].L, lsum[cb], f[cb]);
+    return any_up;
+}
+
+// States whose reference moved are rescaled before P.V adds into them
+// (ACC * 1 is exact, so every column of the wave may take the product).
+template <int D, int CB>
+__device__ __forceinline__ void rescale_states(State<D> (&st)[CB], const FoldF (&f)[CB])
+{
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int db = 0; db < Geo<D>::NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                st[cb].acc[db][i] = __fmul_rn(st[cb].acc[db][i], f[cb].gs);
+}
+
+template <int D, int CB, bool MASK>
+__device__ __forceinline__ void prefill_softmax(f32x4 (&s)[CB][Geo<D>::NKB], const Cols<D> (&cols)[CB], int tile,
+                                                float scale_log2, State<D> (&st)[CB],
+                                                bf16x8 (&pf)[CB][Geo<D>::NKS], FoldF (&f)[CB])
+{
+    if (prefill_softmax_stats<D, CB, MASK>(s, cols, tile, scale_log2, st, pf, f))
+        rescale_states<D, CB>(st, f);
 }
 
 // P.V with DG 16-dim blocks in flight at once (independent MFMA chains for

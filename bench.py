@@ -122,10 +122,12 @@ class DecodeBench:
                                  self.scale, True, workspace=self.ws)
 
     def step(self):
+        # reshape_and_cache of the 4 new tokens + decode attention, through kvp_decode_step
         s = self.i % self.S
         self.i += 1
-        self.kvp.reshape_and_cache(self.pool, self.knew[s], self.vnew[s], self.slot_new[s])
-        self.attention(s)
+        self.kvp.kvp_decode_step(self.pool, self.knew[s], self.vnew[s], self.slot_new[s], self.q[s], self.out,
+                                 self.Hq, self.bt[s], self.sl, self.qsl, 1, self.L, self.scale, True,
+                                 workspace=self.ws)
 
     def attention_only(self):
         s = self.i % self.S
@@ -316,8 +318,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "decode B4 Q1 KV7168 Hq8 Hkv2 Dh128 page16 (random page permutation), "
-                               "%d rotating page sets over a %.2f GB pool; step = reshape_and_cache of the 4 new "
-                               "tokens + split-KV decode" % (dec.S, dec.S * dec.kv_bytes / 1e9),
+                               "%d rotating page sets over a %.2f GB pool; step = kvp_decode_step: reshape_and_cache of "
+                               "the 4 new tokens + split-KV decode (cache write fused into the partial kernel)"
+                               % (dec.S, dec.S * dec.kv_bytes / 1e9),
                    "global_batch": dec.B, "seq_len": dec.L, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(dec.algo_bytes / (attn_us * 1e-6) / 1e9, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -189,6 +189,27 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
                     int32_t max_query_len, int32_t max_seq_len, float scale, int causal,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kvp_decode_step -- reshape_and_cache followed by paged_attention
+ * ("test(rocm): ReshapeAndCache->PagedAttention composition at real dims",
+ * What changed: the cache write and the attention that reads it), with the
+ * same arguments, checks and results as the two calls in that order on
+ * `stream` (the pool ends up with the same bits, `out` gets the same bits).
+ * When only the split-KV path runs (max_query_len * G <= 16) and num_tokens
+ * <= 64, both happen in the split-KV partial launch: the partial kernel
+ * scatters the new rows into the pool and, for keys whose slot is written by
+ * this call, reads the new rows instead of the pool.  Otherwise the cache
+ * kernel runs first.  Duplicate slots and slots beyond the pool follow
+ * reshape_and_cache's rules.
+ */
+int kvp_decode_step(const kvp_pool *pool, const void *k, const void *v, int64_t num_tokens,
+                    int64_t k_token_stride, int64_t v_token_stride, const int64_t *slot_mapping,
+                    const void *q, int64_t q_token_stride, void *out, int64_t out_token_stride,
+                    int32_t num_q_heads, int32_t num_seqs, const int32_t *block_tables,
+                    int32_t block_table_stride, const int32_t *seq_lens, const int32_t *query_start_loc,
+                    int32_t max_query_len, int32_t max_seq_len, float scale, int causal,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Dispatch counters: evidence of which kernel actually ran. */
 typedef struct {
     uint64_t reshape_and_cache_launches;
@@ -196,6 +217,7 @@ typedef struct {
     uint64_t prefill_launches;         /* streaming prefill kernel */
     uint64_t workspace_init_launches;
     uint64_t last_grid_blocks;         /* workgroups of the most recent launch */
+    uint64_t fused_decode_steps;       /* kvp_decode_step calls done in one partial launch */
 } kvp_counters;
 
 int kvp_get_counters(kvp_counters *out);

@@ -44,7 +44,7 @@ class PoolDesc(ctypes.Structure):
 class Counters(ctypes.Structure):
     _fields_ = [("reshape_and_cache_launches", ctypes.c_uint64), ("split_kv_launches", ctypes.c_uint64),
                 ("prefill_launches", ctypes.c_uint64), ("workspace_init_launches", ctypes.c_uint64),
-                ("last_grid_blocks", ctypes.c_uint64)]
+                ("last_grid_blocks", ctypes.c_uint64), ("fused_decode_steps", ctypes.c_uint64)]
 
 
 def load_library(path: str = LIB_PATH):
@@ -68,6 +68,8 @@ def load_library(path: str = LIB_PATH):
         "kvp_workspace_init": ([P, SZ, P], I),
         "paged_attention": ([P, P, I64, P, I64, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P,
                              ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I, P, SZ, P], I),
+        "kvp_decode_step": ([P, P, P, I64, I64, I64, P, P, I64, P, I64, ctypes.c_int32, ctypes.c_int32, P,
+                             ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I, P, SZ, P], I),
         "kvp_get_counters": ([ctypes.POINTER(Counters)], I),
         "kvp_reset_counters": ([], I),
         "kvp_last_error": ([], ctypes.c_char_p),
@@ -227,6 +229,24 @@ def paged_attention(pool: KVPool, q, out, num_q_heads: int, block_tables, seq_le
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().paged_attention(
         pool.handle, _ptr(q), int(q.stride(0)), _ptr(out), int(out.stride(0)), int(num_q_heads), B,
+        _ptr(block_tables), int(block_tables.stride(0)), _ptr(seq_lens), _ptr(query_start_loc),
+        int(max_query_len), int(max_seq_len), float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def kvp_decode_step(pool: KVPool, k, v, slot_mapping, q, out, num_q_heads: int, block_tables, seq_lens,
+                    query_start_loc, max_query_len: int, max_seq_len: int, scale: float | None = None,
+                    causal: bool = True, workspace=None, stream=None) -> None:
+    """reshape_and_cache(pool, k, v, slot_mapping) then paged_attention(...), one launch when possible
+    (see include/kvp.h)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.head_dim)
+    T = int(slot_mapping.shape[0])
+    B = int(seq_lens.shape[0])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().kvp_decode_step(
+        pool.handle, _ptr(k), _ptr(v), T, int(k.stride(0)), int(v.stride(0)), _ptr(slot_mapping),
+        _ptr(q), int(q.stride(0)), _ptr(out), int(out.stride(0)), int(num_q_heads), B,
         _ptr(block_tables), int(block_tables.stride(0)), _ptr(seq_lens), _ptr(query_start_loc),
         int(max_query_len), int(max_seq_len), float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
         _stream(stream)))

@@ -657,7 +657,32 @@ __device__ __forceinline__ void tile_pv(const char *vl, const bf16x8 (&pf)[CB][G
 // across waves through LDS in exactly the order the single-wave tile step
 // uses (max is exact; the sum tree's first levels are the per-wave sums), so
 // the tile's (m, l, acc) are bitwise those of the prefill tile step.
+// Scatter of the new tokens' kv head kvh into the pool (the decode step's
+// cache write, done by workgroup (0, kvh, 0) of the partial launch): the same
+// bit copy as the cache kernel, slots < 0 or beyond the pool skipped.
 template <int D>
+__device__ __forceinline__ void scatter_new_tokens(const AttnArgs &a, int kvh)
+{
+    uint16_t *kc = const_cast<uint16_t *>(a.k_cache), *vc = const_cast<uint16_t *>(a.v_cache);
+    const int64_t hoff = (int64_t)kvh * BS * D;
+    for (int u = threadIdx.x; u < a.num_new * (D / 8); u += NT) {
+        const int i = u / (D / 8), du = u % (D / 8);
+        const int64_t sl = a.new_slots[i];
+        if (sl < 0 || sl >= a.num_blocks * BS)
+            continue;
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(a.new_k + i * a.new_k_stride + (int64_t)kvh * D + du * 8);
+        *reinterpret_cast<u32x4 *>(kc + (sl / BS) * a.k_block_stride + hoff + du * (BS * 8) + (sl % BS) * 8) = val;
+    }
+    for (int u = threadIdx.x; u < a.num_new * D; u += NT) {
+        const int i = u / D, d = u % D;
+        const int64_t sl = a.new_slots[i];
+        if (sl < 0 || sl >= a.num_blocks * BS)
+            continue;
+        vc[(sl / BS) * a.v_block_stride + hoff + (int64_t)d * BS + sl % BS] = a.new_v[i * a.new_v_stride + (int64_t)kvh * D + d];
+    }
+}
+
+template <int D, bool FUSE>
 __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
 {
     using G = Geo<D>;
@@ -671,6 +696,10 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     const int tile = blockIdx.x;
     const int kvh = blockIdx.y;
     const int b = blockIdx.z;
+    if (FUSE && tile == 0 && b == 0)
+        scatter_new_tokens<D>(a, kvh);
+    // new token slots, one per lane (FUSE)
+    const int64_t my_new = (FUSE && (int)(threadIdx.x & 63) < a.num_new) ? a.new_slots[threadIdx.x & 63] : -1;
     // The tile's block-table entries are always inside the padded row
     // (tile < max_tiles), so they are fetched together with the row's
     // metadata instead of after it.
@@ -691,7 +720,42 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     const int64_t hoff = (int64_t)kvh * BS * D;
 
 
-    // ---- issue every load of this workgroup up front (no load is conditional)
+    // ---- new tokens of this launch that land in this tile (FUSE): their
+    // keys are read from the new rows instead of the pool
+    int knew[KPW], vnew[G::NKS], vel[G::NKS];
+#pragma unroll
+    for (int kl = 0; kl < KPW; ++kl)
+        knew[kl] = -1;
+#pragma unroll
+    for (int st = 0; st < G::NKS; ++st)
+        vnew[st] = -1, vel[st] = 0;
+    if (FUSE) {
+        for (int j = a.num_new - 1; j >= 0; --j) {        // the first matching token wins
+            const int64_t sj = ((int64_t)__builtin_amdgcn_readlane((int)(my_new >> 32), j) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)my_new, j);
+            if (sj < 0 || sj >= a.num_blocks * BS)
+                continue;
+            const int64_t bj = sj / BS;
+            const int tj = (int)(sj % BS);
+#pragma unroll
+            for (int kl = 0; kl < KPW; ++kl) {
+                const int kb = w * KPW + kl;
+                const int st = kb >> 1, e = kb & 1;
+                const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
+                const int64_t bk = (c >> 3) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
+                knew[kl] = (bk == bj && tok == tj) ? j : knew[kl];
+            }
+#pragma unroll
+            for (int st = 0; st < G::NKS; ++st) {
+                const int64_t bv = (g >> 1) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
+                const bool hit = bv == bj && (tj >> 3) == (g & 1);
+                vnew[st] = hit ? j : vnew[st];
+                vel[st] = hit ? (tj & 7) : vel[st];
+            }
+        }
+    }
+
+    // ---- issue every load of this workgroup up front
     Cols<D> cols;
     const ColInfo ci = col_info(a, c, kvh, q0, q_len, seq_len);
     load_q<D>(cols, a, ci);
@@ -703,21 +767,46 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
         const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
         const int64_t bk = (c >> 3) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
         const uint16_t *pg = a.k_cache + bk * a.k_block_stride + hoff + tok * 8 + g * 128;
+        int64_t step = 512;                                 // pool: 4 16-byte dim groups per 32 dims
+        if (FUSE && knew[kl] >= 0) {
+            pg = a.new_k + knew[kl] * a.new_k_stride + (int64_t)kvh * D + g * 8;
+            step = 32;                                      // new row: dims contiguous
+        }
 #pragma unroll
         for (int ds = 0; ds < G::NDS; ++ds)
-            kf[kl][ds] = *reinterpret_cast<const bf16x8 *>(pg + ds * 512);
+            kf[kl][ds] = *reinterpret_cast<const bf16x8 *>(pg + ds * step);
     }
     u32x4 vraw[DPW][G::NKS];
+    uint16_t vrep[DPW][G::NKS];
 #pragma unroll
     for (int st = 0; st < G::NKS; ++st) {
         const int64_t bv = (g >> 1) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
         const uint16_t *pg = a.v_cache + bv * a.v_block_stride + hoff + 8 * (g & 1) + c * 16;
 #pragma unroll
-        for (int dl = 0; dl < DPW; ++dl)
+        for (int dl = 0; dl < DPW; ++dl) {
             vraw[dl][st] = *reinterpret_cast<const u32x4 *>(pg + (16 * (w * DPW + dl)) * 16);
+            if (FUSE)
+                vrep[dl][st] = vnew[st] >= 0 ? a.new_v[vnew[st] * a.new_v_stride + (int64_t)kvh * D +
+                                                       16 * (w * DPW + dl) + c]
+                                             : 0;
+        }
     }
     // keep every load above ahead of the first use of any of them
     __builtin_amdgcn_sched_barrier(0);
+    if (FUSE) {
+#pragma unroll
+        for (int st = 0; st < G::NKS; ++st) {
+            if (vnew[st] < 0)
+                continue;
+            const int word = vel[st] >> 1, sh = (vel[st] & 1) * 16;
+#pragma unroll
+            for (int dl = 0; dl < DPW; ++dl)
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd)
+                    if (wd == word)
+                        vraw[dl][st][wd] = (vraw[dl][st][wd] & ~(0xFFFFu << sh)) | ((uint32_t)vrep[dl][st] << sh);
+        }
+    }
     bf16x8 vf[DPW][G::NKS];
 #pragma unroll
     for (int st = 0; st < G::NKS; ++st) {
@@ -1580,12 +1669,15 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
 }
 
 template <int D>
-static hipError_t split_launch(const AttnArgs &a, int max_query_len, hipStream_t s, uint64_t *blocks)
+static hipError_t split_launch(const AttnArgs &a, int max_query_len, hipStream_t s, uint64_t *blocks, bool fuse)
 {
     if (a.max_tiles <= 0 || a.num_seqs <= 0)
         return hipSuccess;
     const dim3 grid((unsigned)a.max_tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    hipLaunchKernelGGL((split_partial_kernel<D>), grid, dim3(NT), 0, s, a);
+    if (fuse)
+        hipLaunchKernelGGL((split_partial_kernel<D, true>), grid, dim3(NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((split_partial_kernel<D, false>), grid, dim3(NT), 0, s, a);
     // one fold workgroup per (column that can exist, 64-dim slice)
     const int max_cols = min(kSplitCols, max_query_len * a.group);
     const dim3 fgrid((unsigned)(max_cols * (D / kFoldSlice)), (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
@@ -1597,9 +1689,21 @@ static hipError_t split_launch(const AttnArgs &a, int max_query_len, hipStream_t
 hipError_t launch_split_kv(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks)
 {
     switch (head_dim) {
-    case 128: return split_launch<128>(a, max_query_len, s, blocks);
-    case 256: return split_launch<256>(a, max_query_len, s, blocks);
-    case 512: return split_launch<512>(a, max_query_len, s, blocks);
+    case 128: return split_launch<128>(a, max_query_len, s, blocks, false);
+    case 256: return split_launch<256>(a, max_query_len, s, blocks, false);
+    case 512: return split_launch<512>(a, max_query_len, s, blocks, false);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_split_kv_fused(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks)
+{
+    if (a.num_new > kMaxFusedTokens)
+        return hipErrorInvalidValue;
+    switch (head_dim) {
+    case 128: return split_launch<128>(a, max_query_len, s, blocks, true);
+    case 256: return split_launch<256>(a, max_query_len, s, blocks, true);
+    case 512: return split_launch<512>(a, max_query_len, s, blocks, true);
     default: return hipErrorInvalidValue;
     }
 }

@@ -21,7 +21,7 @@ namespace {
 thread_local std::string g_err;
 
 std::atomic<uint64_t> g_cache_launches{0}, g_split_launches{0}, g_prefill_launches{0},
-    g_init_launches{0}, g_last_grid{0};
+    g_init_launches{0}, g_last_grid{0}, g_fused_steps{0};
 
 int fail(int code, const char *fmt, ...)
 {
@@ -50,6 +50,191 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 int64_t page_elems(const kvp_pool_desc &d) { return (int64_t)d.num_kv_heads * KVP_BLOCK_SIZE * d.head_dim; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- reshape_and_cache: checks (nothing submitted) and launch
+int prepare_cache(const kvp_pool *pool, const void *k, const void *v, int64_t num_tokens, int64_t k_token_stride,
+                  int64_t v_token_stride, const int64_t *slot_mapping, kvp::CacheArgs &a)
+{
+    if (!pool)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: null pool");
+    const kvp_pool_desc &d = pool->d;
+    if (num_tokens < 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: negative num_tokens");
+    if (num_tokens == 0)
+        return KVP_OK;
+    if (!k || !v || !slot_mapping)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: null pointer");
+    if (!aligned16(k) || !aligned16(v))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: k and v must be 16-byte aligned");
+    const int64_t row = (int64_t)d.num_kv_heads * d.head_dim;
+    if (k_token_stride < row || v_token_stride < row || k_token_stride % 8 || v_token_stride % 8)
+        return fail(KVP_ERR_INVALID_ARGUMENT,
+                    "reshape_and_cache: token strides must be >= %lld and multiples of 8", (long long)row);
+    if (num_tokens > ((int64_t)1 << 40) / row)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: num_tokens too large");
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.num_tokens = num_tokens;
+    a.k_token_stride = k_token_stride;
+    a.v_token_stride = v_token_stride;
+    a.slot_mapping = slot_mapping;
+    a.k_cache = (uint16_t *)d.k_cache;
+    a.v_cache = (uint16_t *)d.v_cache;
+    a.k_block_stride = d.k_block_stride;
+    a.v_block_stride = d.v_block_stride;
+    a.num_blocks = d.num_blocks;
+    a.num_kv_heads = d.num_kv_heads;
+    a.head_dim = d.head_dim;
+    return KVP_OK;
+}
+
+int launch_cache(const kvp::CacheArgs &a, void *stream)
+{
+    uint64_t blocks = 0;
+    hipError_t e = kvp::launch_reshape_and_cache(a, (hipStream_t)stream, &blocks);
+    if (e != hipSuccess)
+        return hip_fail(e, "reshape_and_cache launch");
+    g_cache_launches++;
+    g_last_grid = blocks;
+    return ok();
+}
+
+// ---- paged_attention: checks and path choice (nothing submitted), launch
+struct AttnPlan {
+    bool noop, split, prefill;
+    int D, max_query_len;
+};
+
+int prepare_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride, void *out,
+                      int64_t out_token_stride, int32_t num_q_heads, int32_t num_seqs,
+                      const int32_t *block_tables, int32_t block_table_stride, const int32_t *seq_lens,
+                      const int32_t *query_start_loc, int32_t max_query_len, int32_t max_seq_len, float scale,
+                      int causal, void *workspace, size_t workspace_bytes, kvp::AttnArgs &a, AttnPlan &plan)
+{
+    plan.noop = true;
+    plan.split = plan.prefill = false;
+    if (!pool)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: null pool");
+    const kvp_pool_desc &d = pool->d;
+    const int D = d.head_dim;
+    if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
+        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_q_heads %d not a multiple of num_kv_heads %d",
+                    num_q_heads, d.num_kv_heads);
+    const int G = num_q_heads / d.num_kv_heads;
+    if (G > kvp::kSplitCols)
+        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: group size %d > %d", G, kvp::kSplitCols);
+    if (num_seqs < 0 || max_query_len < 0 || max_seq_len < 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: negative size");
+    if (max_query_len > max_seq_len)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: max_query_len %d > max_seq_len %d", max_query_len,
+                    max_seq_len);
+    if (causal != 0 && causal != 1)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: causal must be 0 or 1");
+    if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(scale * 1.44269504088896340736f))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: scale must be positive and finite");
+    if (num_seqs == 0 || max_query_len == 0)
+        return KVP_OK;
+    if (!q || !out || !block_tables || !seq_lens || !query_start_loc)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: null pointer");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: q and out must be 16-byte aligned");
+    const int64_t row = (int64_t)num_q_heads * D;
+    if (q_token_stride < row || out_token_stride < row || q_token_stride % 8 || out_token_stride % 8)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: token strides must be >= %lld and multiples of 8",
+                    (long long)row);
+    if (block_table_stride < cdiv(max_seq_len, KVP_BLOCK_SIZE) || block_table_stride % 8)
+        return fail(KVP_ERR_INVALID_ARGUMENT,
+                    "paged_attention: block_table_stride %d must be a multiple of 8 and >= %lld pages",
+                    block_table_stride, (long long)cdiv(max_seq_len, KVP_BLOCK_SIZE));
+    if (((uintptr_t)block_tables & 31u) != 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: block_tables must be 32-byte aligned");
+
+    const int T = kvp::tile_tokens(D);
+    a.q = (const uint16_t *)q;
+    a.out = (uint16_t *)out;
+    a.k_cache = (const uint16_t *)d.k_cache;
+    a.v_cache = (const uint16_t *)d.v_cache;
+    a.k_block_stride = d.k_block_stride;
+    a.v_block_stride = d.v_block_stride;
+    a.num_blocks = d.num_blocks;
+    a.q_token_stride = q_token_stride;
+    a.out_token_stride = out_token_stride;
+    a.block_tables = block_tables;
+    a.bt_stride = block_table_stride;
+    a.seq_lens = seq_lens;
+    a.qsl = query_start_loc;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = d.num_kv_heads;
+    a.group = G;
+    a.max_seq_len = max_seq_len;
+    a.max_tiles = (int32_t)cdiv(max_seq_len, T);
+    a.col_groups = 0;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    a.causal = causal;
+    a.ws_acc = a.ws_m = a.ws_l = nullptr;
+    a.split_cols = 0;
+    a.new_k = a.new_v = nullptr;
+    a.new_k_stride = a.new_v_stride = 0;
+    a.new_slots = nullptr;
+    a.num_new = 0;
+
+    // Rows with q_len * G <= 16 (decode, short suffixes) take the split-KV
+    // path, which spreads their KV tiles over the chip; the rest stream
+    // through a prefill kernel.  A call with only such rows needs the
+    // workspace; a mixed batch of several rows uses both paths when a large
+    // enough workspace is given (both paths give the same bits per row).
+    const bool split_only = (int64_t)max_query_len * G <= kvp::kSplitCols;
+    if (num_seqs > 65535 || d.num_kv_heads > 65535)
+        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_seqs and num_kv_heads must be <= 65535");
+    const kvp::Workspace w = kvp::workspace_layout(num_seqs, d.num_kv_heads, a.max_tiles, D);
+    const bool ws_ok = workspace && aligned16(workspace) && workspace_bytes >= w.total;
+    if (split_only) {
+        if (!workspace || !aligned16(workspace))
+            return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: decode needs a 16-byte aligned workspace");
+        if (workspace_bytes < w.total)
+            return fail(KVP_ERR_WORKSPACE_TOO_SMALL, "paged_attention: workspace %zu < %zu bytes", workspace_bytes,
+                        w.total);
+    }
+    const bool use_split = split_only || (num_seqs > 1 && ws_ok);
+    if (use_split) {
+        char *base = (char *)workspace;
+        a.ws_acc = (float *)(base + w.acc_off);
+        a.ws_m = (float *)(base + w.m_off);
+        a.ws_l = (float *)(base + w.l_off);
+    }
+    plan.noop = false;
+    plan.split = use_split;
+    plan.prefill = !split_only;
+    plan.D = D;
+    plan.max_query_len = max_query_len;
+    return KVP_OK;
+}
+
+int launch_attention(kvp::AttnArgs a, const AttnPlan &plan, void *stream)
+{
+    if (plan.split) {
+        uint64_t blocks = 0;
+        hipError_t e = a.num_new > 0 ? kvp::launch_split_kv_fused(a, plan.D, plan.max_query_len, (hipStream_t)stream, &blocks)
+                                     : kvp::launch_split_kv(a, plan.D, plan.max_query_len, (hipStream_t)stream, &blocks);
+        if (e != hipSuccess)
+            return hip_fail(e, "paged_attention split-KV launch");
+        g_split_launches++;
+        if (a.num_new > 0)
+            g_fused_steps++;
+        g_last_grid = blocks;
+        a.split_cols = kvp::kSplitCols;
+    }
+    if (plan.prefill) {
+        uint64_t blocks = 0;
+        hipError_t e = kvp::launch_prefill(a, plan.D, plan.max_query_len, (hipStream_t)stream, &blocks);
+        if (e != hipSuccess)
+            return hip_fail(e, "paged_attention prefill launch");
+        g_prefill_launches++;
+        g_last_grid = blocks;
+    }
+    return ok();
+}
 
 }  // namespace
 
@@ -120,44 +305,11 @@ int reshape_and_cache(const kvp_pool *pool, const void *k, const void *v, int64_
                       int64_t k_token_stride, int64_t v_token_stride, const int64_t *slot_mapping,
                       void *stream)
 {
-    if (!pool)
-        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: null pool");
-    const kvp_pool_desc &d = pool->d;
-    if (num_tokens < 0)
-        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: negative num_tokens");
-    if (num_tokens == 0)
-        return ok();
-    if (!k || !v || !slot_mapping)
-        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: null pointer");
-    if (!aligned16(k) || !aligned16(v))
-        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: k and v must be 16-byte aligned");
-    const int64_t row = (int64_t)d.num_kv_heads * d.head_dim;
-    if (k_token_stride < row || v_token_stride < row || k_token_stride % 8 || v_token_stride % 8)
-        return fail(KVP_ERR_INVALID_ARGUMENT,
-                    "reshape_and_cache: token strides must be >= %lld and multiples of 8", (long long)row);
-    if (num_tokens > ((int64_t)1 << 40) / row)
-        return fail(KVP_ERR_INVALID_ARGUMENT, "reshape_and_cache: num_tokens too large");
     kvp::CacheArgs a;
-    a.k = (const uint16_t *)k;
-    a.v = (const uint16_t *)v;
-    a.num_tokens = num_tokens;
-    a.k_token_stride = k_token_stride;
-    a.v_token_stride = v_token_stride;
-    a.slot_mapping = slot_mapping;
-    a.k_cache = (uint16_t *)d.k_cache;
-    a.v_cache = (uint16_t *)d.v_cache;
-    a.k_block_stride = d.k_block_stride;
-    a.v_block_stride = d.v_block_stride;
-    a.num_blocks = d.num_blocks;
-    a.num_kv_heads = d.num_kv_heads;
-    a.head_dim = d.head_dim;
-    uint64_t blocks = 0;
-    hipError_t e = kvp::launch_reshape_and_cache(a, (hipStream_t)stream, &blocks);
-    if (e != hipSuccess)
-        return hip_fail(e, "reshape_and_cache launch");
-    g_cache_launches++;
-    g_last_grid = blocks;
-    return ok();
+    const int rc = prepare_cache(pool, k, v, num_tokens, k_token_stride, v_token_stride, slot_mapping, a);
+    if (rc != KVP_OK || num_tokens == 0)
+        return rc == KVP_OK ? ok() : rc;
+    return launch_cache(a, stream);
 }
 
 int32_t kvp_padded_width(int32_t width)
@@ -234,109 +386,54 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
                     const int32_t *query_start_loc, int32_t max_query_len, int32_t max_seq_len, float scale,
                     int causal, void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (!pool)
-        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: null pool");
-    const kvp_pool_desc &d = pool->d;
-    const int D = d.head_dim;
-    if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
-        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_q_heads %d not a multiple of num_kv_heads %d",
-                    num_q_heads, d.num_kv_heads);
-    const int G = num_q_heads / d.num_kv_heads;
-    if (G > kvp::kSplitCols)
-        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: group size %d > %d", G, kvp::kSplitCols);
-    if (num_seqs < 0 || max_query_len < 0 || max_seq_len < 0)
-        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: negative size");
-    if (max_query_len > max_seq_len)
-        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: max_query_len %d > max_seq_len %d", max_query_len,
-                    max_seq_len);
-    if (causal != 0 && causal != 1)
-        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: causal must be 0 or 1");
-    if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(scale * 1.44269504088896340736f))
-        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: scale must be positive and finite");
-    if (num_seqs == 0 || max_query_len == 0)
-        return ok();
-    if (!q || !out || !block_tables || !seq_lens || !query_start_loc)
-        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: null pointer");
-    if (!aligned16(q) || !aligned16(out))
-        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: q and out must be 16-byte aligned");
-    const int64_t row = (int64_t)num_q_heads * D;
-    if (q_token_stride < row || out_token_stride < row || q_token_stride % 8 || out_token_stride % 8)
-        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: token strides must be >= %lld and multiples of 8",
-                    (long long)row);
-    if (block_table_stride < cdiv(max_seq_len, KVP_BLOCK_SIZE) || block_table_stride % 8)
-        return fail(KVP_ERR_INVALID_ARGUMENT,
-                    "paged_attention: block_table_stride %d must be a multiple of 8 and >= %lld pages",
-                    block_table_stride, (long long)cdiv(max_seq_len, KVP_BLOCK_SIZE));
-    if (((uintptr_t)block_tables & 31u) != 0)
-        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: block_tables must be 32-byte aligned");
-
-    const int T = kvp::tile_tokens(D);
     kvp::AttnArgs a;
-    a.q = (const uint16_t *)q;
-    a.out = (uint16_t *)out;
-    a.k_cache = (const uint16_t *)d.k_cache;
-    a.v_cache = (const uint16_t *)d.v_cache;
-    a.k_block_stride = d.k_block_stride;
-    a.v_block_stride = d.v_block_stride;
-    a.num_blocks = d.num_blocks;
-    a.q_token_stride = q_token_stride;
-    a.out_token_stride = out_token_stride;
-    a.block_tables = block_tables;
-    a.bt_stride = block_table_stride;
-    a.seq_lens = seq_lens;
-    a.qsl = query_start_loc;
-    a.num_seqs = num_seqs;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = d.num_kv_heads;
-    a.group = G;
-    a.max_seq_len = max_seq_len;
-    a.max_tiles = (int32_t)cdiv(max_seq_len, T);
-    a.col_groups = 0;
-    a.scale_log2 = scale * 1.44269504088896340736f;
-    a.causal = causal;
-    a.ws_acc = a.ws_m = a.ws_l = nullptr;
-    a.split_cols = 0;
+    AttnPlan plan;
+    const int rc = prepare_attention(pool, q, q_token_stride, out, out_token_stride, num_q_heads, num_seqs,
+                                     block_tables, block_table_stride, seq_lens, query_start_loc, max_query_len,
+                                     max_seq_len, scale, causal, workspace, workspace_bytes, a, plan);
+    if (rc != KVP_OK)
+        return rc;
+    if (plan.noop)
+        return ok();
+    return launch_attention(a, plan, stream);
+}
 
-    // Rows with q_len * G <= 16 (decode, short suffixes) take the split-KV
-    // path, which spreads their KV tiles over the chip; the rest stream
-    // through a prefill kernel.  A call with only such rows needs the
-    // workspace; a mixed batch of several rows uses both paths when a large
-    // enough workspace is given (both paths give the same bits per row).
-    const bool split_only = (int64_t)max_query_len * G <= kvp::kSplitCols;
-    if (num_seqs > 65535 || d.num_kv_heads > 65535)
-        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_seqs and num_kv_heads must be <= 65535");
-    const kvp::Workspace w = kvp::workspace_layout(num_seqs, d.num_kv_heads, a.max_tiles, D);
-    const bool ws_ok = workspace && aligned16(workspace) && workspace_bytes >= w.total;
-    if (split_only) {
-        if (!workspace || !aligned16(workspace))
-            return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention: decode needs a 16-byte aligned workspace");
-        if (workspace_bytes < w.total)
-            return fail(KVP_ERR_WORKSPACE_TOO_SMALL, "paged_attention: workspace %zu < %zu bytes", workspace_bytes,
-                        w.total);
+int kvp_decode_step(const kvp_pool *pool, const void *k, const void *v, int64_t num_tokens, int64_t k_token_stride,
+                    int64_t v_token_stride, const int64_t *slot_mapping, const void *q, int64_t q_token_stride,
+                    void *out, int64_t out_token_stride, int32_t num_q_heads, int32_t num_seqs,
+                    const int32_t *block_tables, int32_t block_table_stride, const int32_t *seq_lens,
+                    const int32_t *query_start_loc, int32_t max_query_len, int32_t max_seq_len, float scale,
+                    int causal, void *workspace, size_t workspace_bytes, void *stream)
+{
+    kvp::CacheArgs ca;
+    int rc = prepare_cache(pool, k, v, num_tokens, k_token_stride, v_token_stride, slot_mapping, ca);
+    if (rc != KVP_OK)
+        return rc;
+    kvp::AttnArgs a;
+    AttnPlan plan;
+    rc = prepare_attention(pool, q, q_token_stride, out, out_token_stride, num_q_heads, num_seqs, block_tables,
+                           block_table_stride, seq_lens, query_start_loc, max_query_len, max_seq_len, scale, causal,
+                           workspace, workspace_bytes, a, plan);
+    if (rc != KVP_OK)
+        return rc;
+    // one launch when only the split-KV path runs and the new tokens fit a wave
+    if (!plan.noop && plan.split && !plan.prefill && num_tokens > 0 && num_tokens <= kvp::kMaxFusedTokens) {
+        a.new_k = (const uint16_t *)k;
+        a.new_v = (const uint16_t *)v;
+        a.new_k_stride = k_token_stride;
+        a.new_v_stride = v_token_stride;
+        a.new_slots = slot_mapping;
+        a.num_new = (int32_t)num_tokens;
+        return launch_attention(a, plan, stream);
     }
-    const bool use_split = split_only || (num_seqs > 1 && ws_ok);
-    if (use_split) {
-        char *base = (char *)workspace;
-        a.ws_acc = (float *)(base + w.acc_off);
-        a.ws_m = (float *)(base + w.m_off);
-        a.ws_l = (float *)(base + w.l_off);
-        uint64_t blocks = 0;
-        hipError_t e = kvp::launch_split_kv(a, D, max_query_len, (hipStream_t)stream, &blocks);
-        if (e != hipSuccess)
-            return hip_fail(e, "paged_attention split-KV launch");
-        g_split_launches++;
-        g_last_grid = blocks;
-        a.split_cols = kvp::kSplitCols;
+    if (num_tokens > 0) {
+        rc = launch_cache(ca, stream);
+        if (rc != KVP_OK)
+            return rc;
     }
-    if (!split_only) {
-        uint64_t blocks = 0;
-        hipError_t e = kvp::launch_prefill(a, D, max_query_len, (hipStream_t)stream, &blocks);
-        if (e != hipSuccess)
-            return hip_fail(e, "paged_attention prefill launch");
-        g_prefill_launches++;
-        g_last_grid = blocks;
-    }
-    return ok();
+    if (plan.noop)
+        return ok();
+    return launch_attention(a, plan, stream);
 }
 
 int kvp_get_counters(kvp_counters *out)
@@ -348,6 +445,7 @@ int kvp_get_counters(kvp_counters *out)
     out->prefill_launches = g_prefill_launches.load();
     out->workspace_init_launches = g_init_launches.load();
     out->last_grid_blocks = g_last_grid.load();
+    out->fused_decode_steps = g_fused_steps.load();
     return ok();
 }
 
@@ -356,6 +454,7 @@ int kvp_reset_counters(void)
     g_cache_launches = 0;
     g_split_launches = 0;
     g_prefill_launches = 0;
+    g_fused_steps = 0;
     g_init_launches = 0;
     g_last_grid = 0;
     return ok();

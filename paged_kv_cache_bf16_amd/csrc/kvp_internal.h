@@ -47,7 +47,17 @@ struct AttnArgs {
     // split-KV workspace
     float *ws_acc;             // [B][Hkv][max_tiles][kSplitCols][D]
     float *ws_m, *ws_l;        // [B][Hkv][max_tiles][kSplitCols]
+    // new tokens written into the pool by the same launch (decode step):
+    // token i's K/V rows, its slot (< 0: none); keys in those slots are read
+    // from these rows, not from the pool
+    const uint16_t *new_k, *new_v;
+    int64_t new_k_stride, new_v_stride;
+    const int64_t *new_slots;
+    int32_t num_new;
 };
+
+// Most new tokens one fused decode step takes (one per lane of a wave).
+constexpr int kMaxFusedTokens = 64;
 
 struct Workspace {
     size_t acc_off, m_off, l_off, total;
@@ -58,6 +68,9 @@ Workspace workspace_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t max_t
 hipError_t launch_reshape_and_cache(const CacheArgs &a, hipStream_t s, uint64_t *blocks);
 // Split-KV path: per-tile partial kernel, then the fold kernel.
 hipError_t launch_split_kv(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks);
+// The same with a.num_new (<= kMaxFusedTokens) tokens scattered into the pool
+// by the partial kernel itself.
+hipError_t launch_split_kv_fused(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks);
 hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s, uint64_t *blocks);
 

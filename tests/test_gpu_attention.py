@@ -175,6 +175,73 @@ def test_mixed_batch_split_and_prefill_paths_agree():
     compare(both, oracle_attention(w, oracle_pool(w)), "mixed batch")
 
 
+def _decode_step_case(seed, lens, Hq, Hkv, D, new_pos, extra_slots=()):
+    """A decode batch plus new K/V rows for the given positions (one per row),
+    optionally followed by extra (slot, k, v) rows."""
+    w = wl.random_case(seed, lens, [1] * len(lens), Hq, Hkv, D)
+    rng = np.random.default_rng(seed + 7)
+    slots = [int(w.block_tables[b, p // 16]) * 16 + p % 16 for b, p in enumerate(new_pos)]
+    slots += list(extra_slots)
+    T = len(slots)
+    kn = wl.to_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    vn = wl.to_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    return w, np.array(slots, np.int64), kn, vn
+
+
+def _run_step(w, slots, kn, vn, fused):
+    from harness import dev_bits
+    g = GpuCase(w)
+    k, v = dev_bits(kn), dev_bits(vn)
+    sd = torch.from_numpy(slots).cuda()
+    ms = int(w.seq_lens.max())
+    g.out.fill_(-1)
+    torch.cuda.synchronize()
+    before = kvp.kvp_get_counters()
+    if fused:
+        kvp.kvp_decode_step(g.pool, k, v, sd, g.q, g.out, w.num_q_heads, g.bt, g.seq_lens, g.qsl, 1, ms, w.scale,
+                            True, workspace=g.ws)
+    else:
+        kvp.reshape_and_cache(g.pool, k, v, sd)
+        kvp.paged_attention(g.pool, g.q, g.out, w.num_q_heads, g.bt, g.seq_lens, g.qsl, 1, ms, w.scale, True,
+                            workspace=g.ws)
+    torch.cuda.synchronize()
+    after = kvp.kvp_get_counters()
+    delta = {k: after[k] - before[k] for k in ("fused_decode_steps", "reshape_and_cache_launches")}
+    return (g.out.cpu().numpy().view(np.uint16).copy(), g.pool.storage.cpu().numpy().view(np.uint16).copy(),
+            delta)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 2), (256, 8, 2), (512, 16, 2)])
+def test_decode_step_fused_equals_cache_then_attention(D, Hq, Hkv):
+    """kvp_decode_step in one launch: the same pool bits and output bits as
+    reshape_and_cache followed by paged_attention, with the new tokens at the
+    last position, inside a middle tile, at the first key, skipped (-1) and
+    beyond the pool."""
+    lens = [700, 129, 2000, 1]
+    w, slots, kn, vn = _decode_step_case(D + Hq, lens, Hq, Hkv, D, [699, 64, 1000, 0], extra_slots=(-1, 1 << 40))
+    out_f, pool_f, delta = _run_step(w, slots, kn, vn, fused=True)
+    assert delta == {"fused_decode_steps": 1, "reshape_and_cache_launches": 0}
+    out_s, pool_s, _ = _run_step(w, slots, kn, vn, fused=False)
+    bitwise(pool_f, pool_s, "pool after the fused step")
+    bitwise(out_f, out_s, "output of the fused step")
+    assert np.isfinite(bf16_to_f32(out_f)).all()
+
+
+def test_decode_step_many_tokens_falls_back_to_two_launches():
+    lens = [300, 520]
+    w, slots, kn, vn = _decode_step_case(11, lens, 8, 2, 128, [299, 519])
+    extra = [s for s in range(16 * int(w.num_blocks - 5), 16 * int(w.num_blocks)) if s not in set(slots.tolist())]
+    slots = np.concatenate([slots, np.array(extra[:70], np.int64)])     # 72 distinct slots
+    rng = np.random.default_rng(3)
+    kn = wl.to_bf16_bits(rng.standard_normal((len(slots), 2, 128)).astype(np.float32))
+    vn = wl.to_bf16_bits(rng.standard_normal((len(slots), 2, 128)).astype(np.float32))
+    out_f, pool_f, delta = _run_step(w, slots, kn, vn, fused=True)
+    assert delta == {"fused_decode_steps": 0, "reshape_and_cache_launches": 1}
+    out_s, pool_s, _ = _run_step(w, slots, kn, vn, fused=False)
+    bitwise(pool_f, pool_s, "pool")
+    bitwise(out_f, out_s, "output")
+
+
 def test_decode_long_rows():
     """Decode rows of 65..157 tiles match the oracle and their prefill rows
     bitwise."""

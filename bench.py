@@ -325,7 +325,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(dec.algo_bytes / (attn_us * 1e-6) / 1e9, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec.algo_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": _sum_or_none(recorded_traffic("split_partial_kernel<128>"),
+                     "traffic": _sum_or_none(recorded_traffic("split_partial_kernel<128,false>"),
                                              recorded_traffic("split_fold_kernel<128>")),
                      "kernel": "split_partial_kernel<128> + split_fold_kernel<128> (one paged_attention call)",
                      "us_per_call": round(attn_us, 3),

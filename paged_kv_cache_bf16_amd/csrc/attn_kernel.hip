@@ -658,8 +658,8 @@ __device__ __forceinline__ void tile_pv(const char *vl, const bf16x8 (&pf)[CB][G
 // uses (max is exact; the sum tree's first levels are the per-wave sums), so
 // the tile's (m, l, acc) are bitwise those of the prefill tile step.
 // Scatter of the new tokens' kv head kvh into the pool (the decode step's
-// cache write, done by workgroup (0, kvh, 0) of the partial launch): the same
-// bit copy as the cache kernel, slots < 0 or beyond the pool skipped.
+// cache write, done by workgroup (max_tiles, kvh, 0) of the partial launch):
+// the same bit copy as the cache kernel, slots < 0 or beyond the pool skipped.
 template <int D>
 __device__ __forceinline__ void scatter_new_tokens(const AttnArgs &a, int kvh)
 {
@@ -696,10 +696,20 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     const int tile = blockIdx.x;
     const int kvh = blockIdx.y;
     const int b = blockIdx.z;
-    if (FUSE && tile == 0 && b == 0)
-        scatter_new_tokens<D>(a, kvh);
-    // new token slots, one per lane (FUSE)
-    const int64_t my_new = (FUSE && (int)(threadIdx.x & 63) < a.num_new) ? a.new_slots[threadIdx.x & 63] : -1;
+    if (FUSE && tile == a.max_tiles) {
+        // the extra column of workgroups writes the new tokens (kv head kvh)
+        if (b == 0)
+            scatter_new_tokens<D>(a, kvh);
+        return;
+    }
+    // new token slots, one per lane (FUSE; num_new >= 1), loaded with the
+    // block ids, before anything waits
+    int64_t my_new = -1;
+    if (FUSE) {
+        const int ln = (int)(threadIdx.x & 63);
+        const int64_t sl = a.new_slots[min(ln, a.num_new - 1)];
+        my_new = ln < a.num_new ? sl : -1;
+    }
     // The tile's block-table entries are always inside the padded row
     // (tile < max_tiles), so they are fetched together with the row's
     // metadata instead of after it.
@@ -720,41 +730,6 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     const int64_t hoff = (int64_t)kvh * BS * D;
 
 
-    // ---- new tokens of this launch that land in this tile (FUSE): their
-    // keys are read from the new rows instead of the pool
-    int knew[KPW], vnew[G::NKS], vel[G::NKS];
-#pragma unroll
-    for (int kl = 0; kl < KPW; ++kl)
-        knew[kl] = -1;
-#pragma unroll
-    for (int st = 0; st < G::NKS; ++st)
-        vnew[st] = -1, vel[st] = 0;
-    if (FUSE) {
-        for (int j = a.num_new - 1; j >= 0; --j) {        // the first matching token wins
-            const int64_t sj = ((int64_t)__builtin_amdgcn_readlane((int)(my_new >> 32), j) << 32) |
-                               (uint32_t)__builtin_amdgcn_readlane((int)my_new, j);
-            if (sj < 0 || sj >= a.num_blocks * BS)
-                continue;
-            const int64_t bj = sj / BS;
-            const int tj = (int)(sj % BS);
-#pragma unroll
-            for (int kl = 0; kl < KPW; ++kl) {
-                const int kb = w * KPW + kl;
-                const int st = kb >> 1, e = kb & 1;
-                const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
-                const int64_t bk = (c >> 3) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
-                knew[kl] = (bk == bj && tok == tj) ? j : knew[kl];
-            }
-#pragma unroll
-            for (int st = 0; st < G::NKS; ++st) {
-                const int64_t bv = (g >> 1) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
-                const bool hit = bv == bj && (tj >> 3) == (g & 1);
-                vnew[st] = hit ? j : vnew[st];
-                vel[st] = hit ? (tj & 7) : vel[st];
-            }
-        }
-    }
-
     // ---- issue every load of this workgroup up front
     Cols<D> cols;
     const ColInfo ci = col_info(a, c, kvh, q0, q_len, seq_len);
@@ -767,44 +742,78 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
         const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
         const int64_t bk = (c >> 3) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
         const uint16_t *pg = a.k_cache + bk * a.k_block_stride + hoff + tok * 8 + g * 128;
-        int64_t step = 512;                                 // pool: 4 16-byte dim groups per 32 dims
-        if (FUSE && knew[kl] >= 0) {
-            pg = a.new_k + knew[kl] * a.new_k_stride + (int64_t)kvh * D + g * 8;
-            step = 32;                                      // new row: dims contiguous
-        }
 #pragma unroll
         for (int ds = 0; ds < G::NDS; ++ds)
-            kf[kl][ds] = *reinterpret_cast<const bf16x8 *>(pg + ds * step);
+            kf[kl][ds] = *reinterpret_cast<const bf16x8 *>(pg + ds * 512);
     }
     u32x4 vraw[DPW][G::NKS];
-    uint16_t vrep[DPW][G::NKS];
 #pragma unroll
     for (int st = 0; st < G::NKS; ++st) {
         const int64_t bv = (g >> 1) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
         const uint16_t *pg = a.v_cache + bv * a.v_block_stride + hoff + 8 * (g & 1) + c * 16;
 #pragma unroll
-        for (int dl = 0; dl < DPW; ++dl) {
+        for (int dl = 0; dl < DPW; ++dl)
             vraw[dl][st] = *reinterpret_cast<const u32x4 *>(pg + (16 * (w * DPW + dl)) * 16);
-            if (FUSE)
-                vrep[dl][st] = vnew[st] >= 0 ? a.new_v[vnew[st] * a.new_v_stride + (int64_t)kvh * D +
-                                                       16 * (w * DPW + dl) + c]
-                                             : 0;
-        }
     }
     // keep every load above ahead of the first use of any of them
     __builtin_amdgcn_sched_barrier(0);
+
+    // ---- new tokens of this launch whose slots fall in this tile (FUSE):
+    // their keys come from the new rows, not from the pool (reloaded only in
+    // the waves that hold such a key)
     if (FUSE) {
+        int knew[KPW], vnew[G::NKS], vel[G::NKS];
+#pragma unroll
+        for (int kl = 0; kl < KPW; ++kl)
+            knew[kl] = -1;
+#pragma unroll
+        for (int st = 0; st < G::NKS; ++st)
+            vnew[st] = -1, vel[st] = 0;
+        for (int jn = a.num_new - 1; jn >= 0; --jn) {       // the first matching token wins
+            const int64_t sj = ((int64_t)__builtin_amdgcn_readlane((int)(my_new >> 32), jn) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)my_new, jn);
+            if (sj < 0 || sj >= a.num_blocks * BS)
+                continue;
+            const int64_t bj = sj / BS;
+            const int tj = (int)(sj % BS);
+#pragma unroll
+            for (int kl = 0; kl < KPW; ++kl) {
+                const int kb = w * KPW + kl;
+                const int st = kb >> 1, e = kb & 1;
+                const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
+                const int64_t bk = (c >> 3) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
+                knew[kl] = (bk == bj && tok == tj) ? jn : knew[kl];
+            }
+#pragma unroll
+            for (int st = 0; st < G::NKS; ++st) {
+                const int64_t bv = (g >> 1) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
+                const bool hit = bv == bj && (tj >> 3) == (g & 1);
+                vnew[st] = hit ? jn : vnew[st];
+                vel[st] = hit ? (tj & 7) : vel[st];
+            }
+        }
+#pragma unroll
+        for (int kl = 0; kl < KPW; ++kl) {
+            if (knew[kl] >= 0) {
+                const uint16_t *row = a.new_k + knew[kl] * a.new_k_stride + (int64_t)kvh * D + g * 8;
+#pragma unroll
+                for (int ds = 0; ds < G::NDS; ++ds)
+                    kf[kl][ds] = *reinterpret_cast<const bf16x8 *>(row + ds * 32);
+            }
+        }
 #pragma unroll
         for (int st = 0; st < G::NKS; ++st) {
-            if (vnew[st] < 0)
-                continue;
-            const int word = vel[st] >> 1, sh = (vel[st] & 1) * 16;
+            if (vnew[st] >= 0) {
+                const int word = vel[st] >> 1, sh = (vel[st] & 1) * 16;
 #pragma unroll
-            for (int dl = 0; dl < DPW; ++dl)
+                for (int dl = 0; dl < DPW; ++dl) {
+                    const uint16_t x = a.new_v[vnew[st] * a.new_v_stride + (int64_t)kvh * D + 16 * (w * DPW + dl) + c];
 #pragma unroll
-                for (int wd = 0; wd < 4; ++wd)
-                    if (wd == word)
-                        vraw[dl][st][wd] = (vraw[dl][st][wd] & ~(0xFFFFu << sh)) | ((uint32_t)vrep[dl][st] << sh);
+                    for (int wd = 0; wd < 4; ++wd)
+                        if (wd == word)
+                            vraw[dl][st][wd] = (vraw[dl][st][wd] & ~(0xFFFFu << sh)) | ((uint32_t)x << sh);
+                }
+            }
         }
     }
     bf16x8 vf[DPW][G::NKS];
@@ -1674,8 +1683,8 @@ static hipError_t split_launch(const AttnArgs &a, int max_query_len, hipStream_t
     if (a.max_tiles <= 0 || a.num_seqs <= 0)
         return hipSuccess;
     const dim3 grid((unsigned)a.max_tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    if (fuse)
-        hipLaunchKernelGGL((split_partial_kernel<D, true>), grid, dim3(NT), 0, s, a);
+    if (fuse)   // one more column of workgroups for the cache write
+        hipLaunchKernelGGL((split_partial_kernel<D, true>), dim3(grid.x + 1, grid.y, grid.z), dim3(NT), 0, s, a);
     else
         hipLaunchKernelGGL((split_partial_kernel<D, false>), grid, dim3(NT), 0, s, a);
     // one fold workgroup per (column that can exist, 64-dim slice)

@@ -46,10 +46,12 @@ def _load():
         lib.oracle_reshape_and_cache.argtypes = [P, P, i64, i32, i32, i64, i64, P, P, i64, i64, i64, P]
         lib.oracle_reshape_and_cache.restype = ctypes.c_int
         lib.oracle_paged_attention.argtypes = [P, P, P, P, i64, i64, i64, P, i32, i32, P, P, i32, i32,
-                                               i32, f32, i32, P, i64]
+                                               i32, f32, i32, P, i64, P]
         lib.oracle_paged_attention.restype = ctypes.c_int
         lib.oracle_prepare_block_tables.argtypes = [P, P, i32, i32, P, i64]
         lib.oracle_prepare_block_tables.restype = ctypes.c_int
+        lib.oracle_merge_states.argtypes = [P, P, P, P, P, P, i64, i32]
+        lib.oracle_merge_states.restype = None
         _lib = lib
     return _lib
 
@@ -110,10 +112,11 @@ def reshape_and_cache(pool: Pool, k: np.ndarray, v: np.ndarray, slot_mapping: np
 
 
 def paged_attention(q: np.ndarray, pool: Pool, block_tables: np.ndarray, seq_lens, query_start_loc,
-                    num_q_heads: int, scale: float, causal: bool = True, rows=None) -> np.ndarray:
+                    num_q_heads: int, scale: float, causal: bool = True, rows=None, return_lse: bool = False):
     """FP32 attention output for the requested query rows (all rows if ``rows`` is None).
 
-    q: [Tq, Hq, D] uint16 BF16 bits.  Returns [n_rows, Hq, D] float32.
+    q: [Tq, Hq, D] uint16 BF16 bits.  Returns [n_rows, Hq, D] float32, and with
+    ``return_lse`` also the [n_rows, Hq] float32 log-sum-exp of the scaled scores.
     """
     q = np.ascontiguousarray(q, dtype=np.uint16)
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
@@ -128,15 +131,38 @@ def paged_attention(q: np.ndarray, pool: Pool, block_tables: np.ndarray, seq_len
         rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
         n = rows_arr.shape[0]
     out = np.empty((n, num_q_heads, pool.head_dim), dtype=np.float32)
+    lse = np.empty((n, num_q_heads), dtype=np.float32) if return_lse else None
     kp, vp = pool._kv_ptrs()
     rc = _load().oracle_paged_attention(_ptr(out), _ptr(q), kp, vp, pool.num_blocks,
                                         pool.k_block_stride, pool.v_block_stride, _ptr(bt), B, W,
                                         _ptr(sl), _ptr(qsl), num_q_heads, pool.num_kv_heads,
                                         pool.head_dim, float(scale), int(bool(causal)),
-                                        None if rows_arr is None else _ptr(rows_arr), n)
+                                        None if rows_arr is None else _ptr(rows_arr), n,
+                                        None if lse is None else _ptr(lse))
     if rc != 0:
         raise OracleError("paged_attention: inconsistent metadata")
-    return out
+    return (out, lse) if return_lse else out
+
+
+def merge_states(out_a, lse_a, out_b, lse_b):
+    """Merge two attention results over disjoint key sets (FP64).
+
+    out_*: [..., D] values (float, or uint16 BF16 bits), lse_*: [...] natural-log
+    LSE.  Returns (out [..., D] float64, lse [...] float64).
+    """
+    def as_f64(x):
+        x = np.asarray(x)
+        return bf16_bits_to_f32(x).astype(np.float64) if x.dtype == np.uint16 else x.astype(np.float64)
+    a, b = np.ascontiguousarray(as_f64(out_a)), np.ascontiguousarray(as_f64(out_b))
+    la = np.ascontiguousarray(np.asarray(lse_a, dtype=np.float64))
+    lb = np.ascontiguousarray(np.asarray(lse_b, dtype=np.float64))
+    assert a.shape == b.shape and la.shape == lb.shape == a.shape[:-1]
+    D = a.shape[-1]
+    n = int(np.prod(la.shape))
+    out = np.empty(a.shape, dtype=np.float64)
+    lse = np.empty(la.shape, dtype=np.float64)
+    _load().oracle_merge_states(_ptr(out), _ptr(lse), _ptr(a), _ptr(la), _ptr(b), _ptr(lb), n, D)
+    return out, lse
 
 
 def prepare_block_tables(block_tables: np.ndarray, seq_lens, num_blocks: int) -> np.ndarray:

@@ -30,6 +30,11 @@
  *     V element at v_pool[b*v_block_stride + h*16*D + d*16 + t]
  *   i.e. a K page is [D/8][16 tokens][8 dims] and a V page is [D][16 tokens].
  *
+ * LSE (log-sum-exp) output [Bitwise R/R, Additional checks: the causal
+ * and LSE results are compared with decode]: the pages name the quantity
+ * only; it is read here as the natural-log log-sum-exp of the scaled scores
+ * a query row sees, lse = m + log(l) with m and l of the softmax below.
+ *
  * Readings where the pages are silent (each listed in the design notes):
  *   - GQA: query head h uses kv head h / (Hq/Hkv).
  *   - Suffix queries are bottom-right aligned: query r of a row with q_len
@@ -130,7 +135,7 @@ static int64_t attend_row(float *out, const uint16_t *qrow, const uint16_t *k_po
                           const uint16_t *v_pool, int64_t k_block_stride, int64_t v_block_stride,
                           const int32_t *bt_row, int64_t seq_len, int64_t q_len, int64_t r,
                           int Hq, int Hkv, int D, float scale, int causal,
-                          float *s /* scratch [seq_len] */)
+                          float *lse /* [Hq] or NULL */, float *s /* scratch [seq_len] */)
 {
     int G = Hq / Hkv;
     int64_t pos = seq_len - q_len + r;               /* bottom-right alignment */
@@ -161,6 +166,9 @@ static int64_t attend_row(float *out, const uint16_t *qrow, const uint16_t *k_po
                 acc += s[j] * v_logical(v_pool, v_block_stride, bt_row, g, j, d, D);
             out[(int64_t)h * D + d] = acc / l;
         }
+        /* log-sum-exp of the scaled scores: log(sum_j exp(s_j)) = m + log(l) */
+        if (lse)
+            lse[h] = m + logf(l);
     }
     return nkeys;
 }
@@ -178,7 +186,7 @@ int oracle_paged_attention(float *out, const uint16_t *q, const uint16_t *k_pool
                            int64_t v_block_stride, const int32_t *block_tables, int B, int W,
                            const int32_t *seq_lens, const int32_t *query_start_loc, int Hq,
                            int Hkv, int D, float scale, int causal, const int64_t *rows,
-                           int64_t n_rows)
+                           int64_t n_rows, float *lse /* [n_rows or Tq][Hq] or NULL */)
 {
     if (Hkv <= 0 || Hq % Hkv != 0)
         return -1;
@@ -225,11 +233,50 @@ int oracle_paged_attention(float *out, const uint16_t *q, const uint16_t *k_pool
             attend_row(out + i * (int64_t)Hq * D, q + row * (int64_t)Hq * D, k_pool, v_pool,
                        k_block_stride, v_block_stride, block_tables + (int64_t)b * W,
                        seq_lens[b], q_len, row - query_start_loc[b], Hq, Hkv, D, scale,
-                       causal, s);
+                       causal, lse ? lse + i * (int64_t)Hq : NULL, s);
         }
         free(s);
     }
     return failed ? -1 : 0;
+}
+
+/*
+ * Merge of two attention results over disjoint key sets of the same query
+ * rows, each given as (output, LSE) [Bitwise R/R, Additional checks: LSE
+ * results].  With M = max(lse_a, lse_b) and weights w = exp(lse - M), the
+ * softmax over the union of the key sets gives
+ *   out = (w_a * out_a + w_b * out_b) / (w_a + w_b),
+ *   lse = M + log(w_a + w_b),
+ * because each side's output is its own exp-weighted mean of V and its LSE
+ * the log of its weight total.  A side with lse = -inf has no keys and
+ * contributes nothing (its output is not read); both empty gives out = 0,
+ * lse = -inf.  FP64 throughout.  Arrays are [n][D] and [n] (n = rows x heads).
+ */
+void oracle_merge_states(double *out, double *lse, const double *out_a, const double *lse_a,
+                         const double *out_b, const double *lse_b, int64_t n, int D)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double la = lse_a[i], lb = lse_b[i];
+        double M = la > lb ? la : lb;
+        if (M == -INFINITY) {
+            for (int d = 0; d < D; ++d)
+                out[i * D + d] = 0.0;
+            lse[i] = -INFINITY;
+            continue;
+        }
+        double wa = la == -INFINITY ? 0.0 : exp(la - M);
+        double wb = lb == -INFINITY ? 0.0 : exp(lb - M);
+        double w = wa + wb;
+        for (int d = 0; d < D; ++d) {
+            double x = 0.0;
+            if (wa != 0.0)
+                x += wa * out_a[i * D + d];
+            if (wb != 0.0)
+                x += wb * out_b[i * D + d];
+            out[i * D + d] = x / w;
+        }
+        lse[i] = M + log(w);
+    }
 }
 
 /*

@@ -352,3 +352,117 @@ def test_prepare_tables_worked_cases():
         oracle.prepare_block_tables(bt, [20, 0, 144], num_blocks=9)
     with pytest.raises(oracle.OracleError):        # table too narrow for seq_len
         oracle.prepare_block_tables(bt, [20, 0, 145], num_blocks=10)
+
+
+# ---------------------------------------------------------------- LSE output and the merge of two results
+
+def _dense_lse_out(q, k, v, scale, visible):
+    """float64 torch reference over dense K/V: q [n,H,D], k/v [L,H,D] (heads already
+    matched), visible [n,L] bool.  Returns (out [n,H,D], lse [n,H]) via torch.logsumexp."""
+    qt, kt, vt = (torch.from_numpy(np.asarray(x, np.float64)).permute(1, 0, 2) for x in (q, k, v))
+    s = torch.matmul(qt, kt.transpose(1, 2)) * scale                  # [H, n, L]
+    s = s.masked_fill(~torch.from_numpy(visible)[None], float("-inf"))
+    lse = torch.logsumexp(s, -1)                                      # [H, n]
+    out = torch.matmul(torch.softmax(s, -1), vt)
+    return out.permute(1, 0, 2).numpy(), lse.T.numpy()
+
+
+def test_oracle_lse_matches_torch_logsumexp():
+    w = wl.random_case(21, [1, 40, 300], [1, 40, 7], 8, 2, 128, causal=True)
+    pool = make_pool(w)
+    oracle.reshape_and_cache(pool, w.k, w.v, w.slot_mapping)
+    out, lse = oracle.paged_attention(w.q, pool, w.block_tables, w.seq_lens, w.query_start_loc,
+                                      w.num_q_heads, w.scale, True, return_lse=True)
+    G = w.num_q_heads // w.num_kv_heads
+    koff = 0
+    for b in range(w.batch):
+        L, n, q0 = int(w.seq_lens[b]), int(w.query_lens[b]), int(w.query_start_loc[b])
+        k = np.repeat(oracle.bf16_bits_to_f32(w.k[koff:koff + L]), G, axis=1)
+        v = np.repeat(oracle.bf16_bits_to_f32(w.v[koff:koff + L]), G, axis=1)
+        koff += L
+        pos = L - n + np.arange(n)
+        vis = np.arange(L)[None] <= pos[:, None]
+        ro, rl = _dense_lse_out(oracle.bf16_bits_to_f32(w.q[q0:q0 + n]), k, v, w.scale, vis)
+        assert np.abs(lse[q0:q0 + n] - rl).max() < 1e-5
+        assert np.abs(out[q0:q0 + n] - ro).max() < 3e-5
+
+
+def test_lse_closed_forms():
+    rng = np.random.default_rng(22)
+    scale = 1 / math.sqrt(128)
+    q, k, v = (_bf(rng.standard_normal(s)) for s in ((1, 1, 128), (1, 1, 128), (1, 1, 128)))
+    L = 1
+    npg = 1
+    pool = oracle.Pool(npg, 1, 128)
+    oracle.reshape_and_cache(pool, wl.to_bf16_bits(k), wl.to_bf16_bits(v), np.array([0]))
+    _, lse = oracle.paged_attention(wl.to_bf16_bits(q), pool, np.zeros((1, 1), np.int32), [L], [0, 1], 1,
+                                    scale, False, return_lse=True)
+    # one key: the LSE is that key's scaled score
+    assert abs(lse[0, 0] - scale * float(q[0, 0].astype(np.float64) @ k[0, 0].astype(np.float64))) < 1e-6
+    # n identical keys: score + log(n)
+    n = 300
+    kk = np.broadcast_to(k, (n, 1, 128)).copy()
+    vv = _bf(rng.standard_normal((n, 1, 128)))
+    npg = (n + 15) // 16
+    pool = oracle.Pool(npg, 1, 128)
+    oracle.reshape_and_cache(pool, wl.to_bf16_bits(kk), wl.to_bf16_bits(vv), np.arange(n))
+    _, lse_n = oracle.paged_attention(wl.to_bf16_bits(q), pool, np.arange(npg, dtype=np.int32)[None], [n],
+                                      [0, 1], 1, scale, False, return_lse=True)
+    assert abs(lse_n[0, 0] - (lse[0, 0] + math.log(n))) < 1e-5
+
+
+def test_merge_of_disjoint_key_sets_is_attention_over_their_union():
+    rng = np.random.default_rng(23)
+    n, H, D, L = 5, 3, 64, 90
+    q, k, v = (rng.standard_normal(s) for s in ((n, H, D), (L, H, D), (L, H, D)))
+    for split in (1, 37, 89):
+        vis = np.ones((n, L), bool)
+        full_o, full_l = _dense_lse_out(q, k, v, 0.2, vis)
+        oa, la = _dense_lse_out(q, k[:split], v[:split], 0.2, vis[:, :split])
+        ob, lb = _dense_lse_out(q, k[split:], v[split:], 0.2, vis[:, split:])
+        mo, ml = oracle.merge_states(oa, la, ob, lb)
+        assert np.abs(mo - full_o).max() < 1e-12 and np.abs(ml - full_l).max() < 1e-12
+        # the order of the two sides does not matter
+        mo2, ml2 = oracle.merge_states(ob, lb, oa, la)
+        assert np.abs(mo2 - mo).max() < 1e-14 and np.abs(ml2 - ml).max() < 1e-14
+
+
+def test_merge_special_cases():
+    rng = np.random.default_rng(24)
+    a = rng.standard_normal((4, 2, 16))
+    la = rng.standard_normal((4, 2)) * 5
+    nan = np.full_like(a, np.nan)
+    ninf = np.full_like(la, -np.inf)
+    # an empty side contributes nothing, whatever its output holds
+    mo, ml = oracle.merge_states(a, la, nan, ninf)
+    np.testing.assert_array_equal(mo, a)
+    np.testing.assert_array_equal(ml, la)
+    mo, ml = oracle.merge_states(nan, ninf, a, la)
+    np.testing.assert_array_equal(mo, a)
+    # both empty: zero output, -inf LSE
+    mo, ml = oracle.merge_states(nan, ninf, nan, ninf)
+    assert (mo == 0).all() and (ml == -np.inf).all()
+    # equal LSE: the mean of the outputs, LSE + log 2
+    b = rng.standard_normal(a.shape)
+    mo, ml = oracle.merge_states(a, la, b, la)
+    np.testing.assert_allclose(mo, (a + b) / 2, rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(ml, la + math.log(2), rtol=1e-15)
+    # a far smaller LSE leaves the other side (up to its weight exp(-diff))
+    mo, ml = oracle.merge_states(a, la, b, la - 60)
+    np.testing.assert_allclose(mo, a, atol=1e-25 + 1e-20 * np.abs(b).max())
+
+
+def test_chunked_prefill_by_merging_prefix_and_chunk():
+    """Prefix keys (all visible, non-causal) merged with the chunk's own keys
+    (causal) equal a causal prefill over the whole row."""
+    w = wl.random_case(25, [96 + 40], [40], 8, 2, 128, causal=True)
+    pool = make_pool(w)
+    oracle.reshape_and_cache(pool, w.k, w.v, w.slot_mapping)
+    full = oracle.paged_attention(w.q, pool, w.block_tables, w.seq_lens, w.query_start_loc,
+                                  w.num_q_heads, w.scale, True)
+    oa, la = oracle.paged_attention(w.q, pool, w.block_tables, [96], [0, 40], w.num_q_heads, w.scale,
+                                    False, return_lse=True)
+    ob, lb = oracle.paged_attention(w.q, pool, w.block_tables[:, 96 // 16:], [40], [0, 40], w.num_q_heads,
+                                    w.scale, True, return_lse=True)
+    mo, _ = oracle.merge_states(oa, la, ob, lb)
+    assert np.abs(mo - full).max() < 3e-6

@@ -190,6 +190,49 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * paged_attention_lse -- paged_attention that also writes, for every query
+ * row and head it computes, the natural-log log-sum-exp of that row's scaled
+ * scores, lse = log(sum_j exp(scale * q.k_j)) over the keys the row sees
+ * ("fix(rocm): stabilize direct paged CK attention for bitwise R/R",
+ * Additional checks: LSE results compared with decode).
+ *   lse   device, FP32, [total_q][num_q_heads] with token stride
+ *         lse_token_stride (elements, >= num_q_heads), 4-byte aligned.
+ * Every other argument, check and result is paged_attention's.  The lse of a
+ * decode row equals bitwise the lse of the prefill row that ends at the same
+ * token.  With kvp_merge_attention, results over disjoint key ranges (for
+ * example a prefix and a new chunk) combine into the result over both.
+ * Errors: those of paged_attention; INVALID_ARGUMENT for a null or
+ * misaligned lse or a short lse_token_stride (nothing submitted).
+ */
+int paged_attention_lse(const kvp_pool *pool, const void *q, int64_t q_token_stride, void *out,
+                        int64_t out_token_stride, float *lse, int64_t lse_token_stride, int32_t num_q_heads,
+                        int32_t num_seqs, const int32_t *block_tables, int32_t block_table_stride,
+                        const int32_t *seq_lens, const int32_t *query_start_loc, int32_t max_query_len,
+                        int32_t max_seq_len, float scale, int causal, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
+ * kvp_merge_attention -- combine two attention results of the same query
+ * rows over disjoint key sets into the result over their union, by the
+ * log-sum-exp identity (the LSE results of "fix(rocm): stabilize direct
+ * paged CK attention for bitwise R/R", Additional checks):
+ *   M = max(lse_a, lse_b), w = exp(lse - M),
+ *   out = (w_a out_a + w_b out_b) / (w_a + w_b),  lse = M + log(w_a + w_b).
+ *   out_a, out_b, out  device, BF16, [num_tokens][num_heads][head_dim]
+ *                      contiguous, 16-byte aligned.
+ *   lse_a, lse_b       device, FP32, [num_tokens][num_heads] contiguous.
+ *   lse                device, same shape, or NULL (not written).
+ * head_dim: a multiple of 8 in [8, 512].  FP32 arithmetic, BF16 RNE output.
+ * A side with lse = -inf has no keys and is ignored (its output row is not
+ * used); both -inf gives out = 0 and lse = -inf.  lse values must not be
+ * NaN or +inf.  out may be out_a or out_b exactly and lse may be lse_a or
+ * lse_b exactly (in-place merge); any other overlap is rejected.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (head_dim), HIP.
+ */
+int kvp_merge_attention(const void *out_a, const float *lse_a, const void *out_b, const float *lse_b, void *out,
+                        float *lse, int64_t num_tokens, int32_t num_heads, int32_t head_dim, void *stream);
+
+/*
  * kvp_decode_step -- reshape_and_cache followed by paged_attention
  * ("test(rocm): ReshapeAndCache->PagedAttention composition at real dims",
  * What changed: the cache write and the attention that reads it), with the
@@ -218,6 +261,7 @@ typedef struct {
     uint64_t workspace_init_launches;
     uint64_t last_grid_blocks;         /* workgroups of the most recent launch */
     uint64_t fused_decode_steps;       /* kvp_decode_step calls done in one partial launch */
+    uint64_t merge_launches;           /* kvp_merge_attention kernels */
 } kvp_counters;
 
 int kvp_get_counters(kvp_counters *out);

@@ -44,7 +44,8 @@ class PoolDesc(ctypes.Structure):
 class Counters(ctypes.Structure):
     _fields_ = [("reshape_and_cache_launches", ctypes.c_uint64), ("split_kv_launches", ctypes.c_uint64),
                 ("prefill_launches", ctypes.c_uint64), ("workspace_init_launches", ctypes.c_uint64),
-                ("last_grid_blocks", ctypes.c_uint64), ("fused_decode_steps", ctypes.c_uint64)]
+                ("last_grid_blocks", ctypes.c_uint64), ("fused_decode_steps", ctypes.c_uint64),
+                ("merge_launches", ctypes.c_uint64)]
 
 
 def load_library(path: str = LIB_PATH):
@@ -68,6 +69,9 @@ def load_library(path: str = LIB_PATH):
         "kvp_workspace_init": ([P, SZ, P], I),
         "paged_attention": ([P, P, I64, P, I64, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P,
                              ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I, P, SZ, P], I),
+        "paged_attention_lse": ([P, P, I64, P, I64, P, I64, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32,
+                                 P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I, P, SZ, P], I),
+        "kvp_merge_attention": ([P, P, P, P, P, P, I64, ctypes.c_int32, ctypes.c_int32, P], I),
         "kvp_decode_step": ([P, P, P, I64, I64, I64, P, P, I64, P, I64, ctypes.c_int32, ctypes.c_int32, P,
                              ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I, P, SZ, P], I),
         "kvp_get_counters": ([ctypes.POINTER(Counters)], I),
@@ -232,6 +236,37 @@ def paged_attention(pool: KVPool, q, out, num_q_heads: int, block_tables, seq_le
         _ptr(block_tables), int(block_tables.stride(0)), _ptr(seq_lens), _ptr(query_start_loc),
         int(max_query_len), int(max_seq_len), float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def paged_attention_lse(pool: KVPool, q, out, lse, num_q_heads: int, block_tables, seq_lens, query_start_loc,
+                        max_query_len: int, max_seq_len: int, scale: float | None = None, causal: bool = True,
+                        workspace=None, stream=None) -> None:
+    """paged_attention that also writes lse[token, head] (float32 device tensor; see include/kvp.h)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.head_dim)
+    B = int(seq_lens.shape[0])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().paged_attention_lse(
+        pool.handle, _ptr(q), int(q.stride(0)), _ptr(out), int(out.stride(0)), _ptr(lse), int(lse.stride(0)),
+        int(num_q_heads), B, _ptr(block_tables), int(block_tables.stride(0)), _ptr(seq_lens),
+        _ptr(query_start_loc), int(max_query_len), int(max_seq_len), float(scale), int(bool(causal)),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvp_merge_attention(out_a, lse_a, out_b, lse_b, out, lse=None, stream=None) -> None:
+    """Merge two results over disjoint key sets: out/lse from (out_a, lse_a) and (out_b, lse_b).
+
+    out_*: [T, H, D] bf16 contiguous device tensors; lse_*: [T, H] float32 (see include/kvp.h)."""
+    T, H, D = (int(x) for x in out_a.shape)
+    for t in (out_a, out_b, out, lse_a, lse_b) + ((lse,) if lse is not None else ()):
+        if not t.is_contiguous():
+            raise ValueError("kvp_merge_attention takes contiguous tensors")
+    if tuple(out_b.shape) != (T, H, D) or tuple(out.shape) != (T, H, D):
+        raise ValueError("kvp_merge_attention: output shapes differ")
+    if tuple(lse_a.shape) != (T, H) or tuple(lse_b.shape) != (T, H) or (lse is not None and tuple(lse.shape) != (T, H)):
+        raise ValueError("kvp_merge_attention: lse shapes must be [T, H]")
+    _check(load_library().kvp_merge_attention(_ptr(out_a), _ptr(lse_a), _ptr(out_b), _ptr(lse_b), _ptr(out),
+                                              _ptr(lse), T, H, D, _stream(stream)))
 
 
 def kvp_decode_step(pool: KVPool, k, v, slot_mapping, q, out, num_q_heads: int, block_tables, seq_lens,

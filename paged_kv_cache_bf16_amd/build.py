@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvp.so")
-SOURCES = ["attn_kernel.hip", "cache_kernel.hip", "kvp_api.cpp"]
+SOURCES = ["attn_kernel.hip", "cache_kernel.hip", "merge_kernel.hip", "kvp_api.cpp"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math",

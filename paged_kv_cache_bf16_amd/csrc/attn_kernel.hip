@@ -269,10 +269,20 @@ __device__ __forceinline__ void load_q(Cols<D> &cf, const AttnArgs &a, const Col
     cf.lim = ci.lim;
 }
 
+// Natural-log log-sum-exp of a column's scaled scores from its final state:
+// sum_j exp2(S_j * scale * log2 e) = 2^R * L, so lse = (R + log2 L) * ln 2.
+// Decode and prefill reach the same (R, L) bits, hence the same lse bits.
+__device__ __forceinline__ float lse_of(float R, float L)
+{
+    return __fmul_rn(__fadd_rn(R, __builtin_amdgcn_logf(L)), 0.693147180559945309f);
+}
+
 template <int D>
 __device__ __forceinline__ void store_out(const AttnArgs &a, const ColInfo &ci, const State<D> &st)
 {
     const int g = (threadIdx.x & 63) >> 4;
+    if (a.lse && g == 0)
+        a.lse[ci.row * a.lse_token_stride + ci.head] = lse_of(st.R, st.L);
     const float inv = 1.0f / st.L;
     uint16_t *dst = a.out + ci.row * a.out_token_stride + (int64_t)ci.head * D + 4 * g;
 #pragma unroll
@@ -1024,6 +1034,8 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
     if (th < kFoldSlice) {
         const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
         a.out[ci.row * a.out_token_stride + (int64_t)ci.head * D + d0 + th] = finish1(acc, 1.0f / L);
+        if (a.lse && slice == 0 && th == 0)
+            a.lse[ci.row * a.lse_token_stride + ci.head] = lse_of(ref_of(M), L);
     }
 }
 

@@ -21,7 +21,7 @@ namespace {
 thread_local std::string g_err;
 
 std::atomic<uint64_t> g_cache_launches{0}, g_split_launches{0}, g_prefill_launches{0},
-    g_init_launches{0}, g_last_grid{0}, g_fused_steps{0};
+    g_init_launches{0}, g_last_grid{0}, g_fused_steps{0}, g_merge_launches{0};
 
 int fail(int code, const char *fmt, ...)
 {
@@ -173,6 +173,8 @@ int prepare_attention(const kvp_pool *pool, const void *q, int64_t q_token_strid
     a.scale_log2 = scale * 1.44269504088896340736f;
     a.causal = causal;
     a.ws_acc = a.ws_m = a.ws_l = nullptr;
+    a.lse = nullptr;
+    a.lse_token_stride = 0;
     a.split_cols = 0;
     a.new_k = a.new_v = nullptr;
     a.new_k_stride = a.new_v_stride = 0;
@@ -398,6 +400,80 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
     return launch_attention(a, plan, stream);
 }
 
+int paged_attention_lse(const kvp_pool *pool, const void *q, int64_t q_token_stride, void *out,
+                        int64_t out_token_stride, float *lse, int64_t lse_token_stride, int32_t num_q_heads,
+                        int32_t num_seqs, const int32_t *block_tables, int32_t block_table_stride,
+                        const int32_t *seq_lens, const int32_t *query_start_loc, int32_t max_query_len,
+                        int32_t max_seq_len, float scale, int causal, void *workspace, size_t workspace_bytes,
+                        void *stream)
+{
+    kvp::AttnArgs a;
+    AttnPlan plan;
+    const int rc = prepare_attention(pool, q, q_token_stride, out, out_token_stride, num_q_heads, num_seqs,
+                                     block_tables, block_table_stride, seq_lens, query_start_loc, max_query_len,
+                                     max_seq_len, scale, causal, workspace, workspace_bytes, a, plan);
+    if (rc != KVP_OK)
+        return rc;
+    if (plan.noop)
+        return ok();
+    if (!lse || ((uintptr_t)lse & 3u) != 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention_lse: lse must be a non-null, 4-byte aligned pointer");
+    if (lse_token_stride < num_q_heads)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "paged_attention_lse: lse_token_stride %lld < num_q_heads %d",
+                    (long long)lse_token_stride, num_q_heads);
+    a.lse = lse;
+    a.lse_token_stride = lse_token_stride;
+    return launch_attention(a, plan, stream);
+}
+
+int kvp_merge_attention(const void *out_a, const float *lse_a, const void *out_b, const float *lse_b, void *out,
+                        float *lse, int64_t num_tokens, int32_t num_heads, int32_t head_dim, void *stream)
+{
+    if (num_tokens < 0 || num_heads <= 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_merge_attention: negative token count or no heads");
+    if (head_dim < 8 || head_dim > 512 || head_dim % 8)
+        return fail(KVP_ERR_UNSUPPORTED, "kvp_merge_attention: head_dim %d must be a multiple of 8 in [8, 512]",
+                    head_dim);
+    if (num_tokens == 0)
+        return ok();
+    if (!out_a || !out_b || !out || !lse_a || !lse_b)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_merge_attention: null pointer");
+    if (!aligned16(out_a) || !aligned16(out_b) || !aligned16(out))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_merge_attention: outputs must be 16-byte aligned");
+    if (((uintptr_t)lse_a | (uintptr_t)lse_b | (uintptr_t)lse) & 3u)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_merge_attention: lse arrays must be 4-byte aligned");
+    const int64_t pairs = num_tokens * num_heads;
+    const int64_t per_block = 4 * (64 / (head_dim / 8));
+    if ((pairs + per_block - 1) / per_block > 0x7fffffff)
+        return fail(KVP_ERR_UNSUPPORTED, "kvp_merge_attention: too many rows");
+    // an output may be one of the inputs exactly, or apart from both
+    auto partial_overlap = [](const void *x, const void *y, int64_t bytes) {
+        const uintptr_t a = (uintptr_t)x, b = (uintptr_t)y;
+        return a != b && a < b + (uintptr_t)bytes && b < a + (uintptr_t)bytes;
+    };
+    const int64_t row_bytes = pairs * head_dim * 2, lse_bytes = pairs * 4;
+    if (partial_overlap(out, out_a, row_bytes) || partial_overlap(out, out_b, row_bytes))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_merge_attention: out partially overlaps an input");
+    if (lse && (partial_overlap(lse, lse_a, lse_bytes) || partial_overlap(lse, lse_b, lse_bytes)))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_merge_attention: lse partially overlaps an input");
+    kvp::MergeArgs m;
+    m.out_a = (const uint16_t *)out_a;
+    m.out_b = (const uint16_t *)out_b;
+    m.lse_a = lse_a;
+    m.lse_b = lse_b;
+    m.out = (uint16_t *)out;
+    m.lse = lse;
+    m.pairs = pairs;
+    m.head_dim = head_dim;
+    uint64_t blocks = 0;
+    const hipError_t e = kvp::launch_merge(m, (hipStream_t)stream, &blocks);
+    if (e != hipSuccess)
+        return hip_fail(e, "kvp_merge_attention launch");
+    g_merge_launches++;
+    g_last_grid = blocks;
+    return ok();
+}
+
 int kvp_decode_step(const kvp_pool *pool, const void *k, const void *v, int64_t num_tokens, int64_t k_token_stride,
                     int64_t v_token_stride, const int64_t *slot_mapping, const void *q, int64_t q_token_stride,
                     void *out, int64_t out_token_stride, int32_t num_q_heads, int32_t num_seqs,
@@ -446,6 +522,7 @@ int kvp_get_counters(kvp_counters *out)
     out->workspace_init_launches = g_init_launches.load();
     out->last_grid_blocks = g_last_grid.load();
     out->fused_decode_steps = g_fused_steps.load();
+    out->merge_launches = g_merge_launches.load();
     return ok();
 }
 
@@ -455,6 +532,7 @@ int kvp_reset_counters(void)
     g_split_launches = 0;
     g_prefill_launches = 0;
     g_fused_steps = 0;
+    g_merge_launches = 0;
     g_init_launches = 0;
     g_last_grid = 0;
     return ok();

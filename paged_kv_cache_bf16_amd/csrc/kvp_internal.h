@@ -44,6 +44,9 @@ struct AttnArgs {
     float scale_log2;          // softmax scale * log2(e), rounded once on the host
     int32_t causal;
     int32_t split_cols;        // prefill kernels skip rows with q_len * G <= split_cols
+    // optional log-sum-exp output [total_q][num_q_heads] (token stride below)
+    float *lse;
+    int64_t lse_token_stride;
     // split-KV workspace
     float *ws_acc;             // [B][Hkv][max_tiles][kSplitCols][D]
     float *ws_m, *ws_l;        // [B][Hkv][max_tiles][kSplitCols]
@@ -73,5 +76,17 @@ hipError_t launch_split_kv(const AttnArgs &a, int head_dim, int max_query_len, h
 hipError_t launch_split_kv_fused(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks);
 hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s, uint64_t *blocks);
+
+// Merge of two (output, lse) results over disjoint key sets; rows are
+// [pairs][head_dim] BF16, lse [pairs] FP32 (lse may be null).
+struct MergeArgs {
+    const uint16_t *out_a, *out_b;
+    const float *lse_a, *lse_b;
+    uint16_t *out;
+    float *lse;
+    int64_t pairs;
+    int32_t head_dim;          // multiple of 8, 8..512
+};
+hipError_t launch_merge(const MergeArgs &m, hipStream_t s, uint64_t *blocks);
 
 }  // namespace kvp

@@ -73,6 +73,19 @@ class GpuCase:
         torch.cuda.synchronize()
         return host_bits(self.out)
 
+    def run_lse(self, causal=None, max_seq_len=None, use_workspace=True):
+        """paged_attention_lse: (output bits, lse float32); rows not computed keep NaN lse."""
+        w = self.w
+        self.out.fill_(-1)
+        lse = torch.full((self.q.shape[0], w.num_q_heads), float("nan"), dtype=torch.float32, device="cuda")
+        ms = int(self.seq_lens_h.max(initial=0)) if max_seq_len is None else int(max_seq_len)
+        kvp.paged_attention_lse(self.pool, self.q, self.out, lse, w.num_q_heads, self.bt, self.seq_lens, self.qsl,
+                                int(self.qlens_h.max(initial=0)), ms, w.scale,
+                                w.causal if causal is None else causal,
+                                workspace=self.ws if use_workspace else None)
+        torch.cuda.synchronize()
+        return host_bits(self.out), lse.cpu().numpy()
+
     def pool_bits(self) -> np.ndarray:
         return host_bits(self.pool.storage)
 

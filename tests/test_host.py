@@ -185,3 +185,51 @@ def test_workspace_bytes_scales_with_tiles(lib):
     a = kvp.kvp_workspace_bytes(pool, 8, 4, 7168)
     b = kvp.kvp_workspace_bytes(pool, 8, 4, 7168 * 2)
     assert a >= 4 * 2 * 56 * 16 * 128 * 4 and b > a
+
+
+@pytest.mark.parametrize("lse,lss,code", [
+    (None, 8, kvp.KVP_ERR_INVALID_ARGUMENT),
+    (0x90000002, 8, kvp.KVP_ERR_INVALID_ARGUMENT),        # not 4-byte aligned
+    (0x90000000, 7, kvp.KVP_ERR_INVALID_ARGUMENT),        # stride < num_q_heads
+])
+def test_attention_lse_rejects_before_launch(lib, lse, lss, code):
+    rc, h = create(lib)
+    kvp.kvp_reset_counters()
+    rc = lib.paged_attention_lse(h, 0x30000000, 8 * 128, 0x40000000, 8 * 128, lse, lss, 8, 1, 0x50000000, 8,
+                                 0x60000000, 0x70000000, 1, 100, 0.1, 1, 0x80000000, 1 << 30, None)
+    assert rc == code
+    c = kvp.kvp_get_counters()
+    assert c["split_kv_launches"] == 0 and c["prefill_launches"] == 0
+    # the checks paged_attention makes come first and are the same
+    assert lib.paged_attention_lse(h, 0x30000000, 8 * 128, 0x40000000, 8 * 128, 0x90000000, 8, 7, 1, 0x50000000,
+                                   8, 0x60000000, 0x70000000, 1, 100, 0.1, 1, 0x80000000, 1 << 30,
+                                   None) == kvp.KVP_ERR_UNSUPPORTED
+    lib.kv_pool_destroy(h)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=12), kvp.KVP_ERR_UNSUPPORTED),
+    (dict(D=1024), kvp.KVP_ERR_UNSUPPORTED),
+    (dict(T=-1), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(H=0), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(a=None), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(lb=None), kvp.KVP_ERR_INVALID_ARGUMENT),
+    (dict(a=0x10000008), kvp.KVP_ERR_INVALID_ARGUMENT),     # rows not 16-byte aligned
+    (dict(lse=0x60000002), kvp.KVP_ERR_INVALID_ARGUMENT),   # lse not 4-byte aligned
+    (dict(out=0x10000010), kvp.KVP_ERR_INVALID_ARGUMENT),   # partial overlap with out_a
+    (dict(lse=0x40000004), kvp.KVP_ERR_INVALID_ARGUMENT),   # partial overlap with lse_a
+])
+def test_merge_rejects_before_launch(lib, kw, code):
+    a = dict(a=0x10000000, la=0x40000000, b=0x20000000, lb=0x50000000, out=0x30000000, lse=0x60000000,
+             T=4, H=8, D=128)
+    a.update(kw)
+    kvp.kvp_reset_counters()
+    rc = lib.kvp_merge_attention(a["a"], a["la"], a["b"], a["lb"], a["out"], a["lse"], a["T"], a["H"], a["D"], None)
+    assert rc == code
+    assert kvp.kvp_get_counters()["merge_launches"] == 0
+
+
+def test_merge_empty_is_ok_without_launch(lib):
+    kvp.kvp_reset_counters()
+    assert lib.kvp_merge_attention(None, None, None, None, None, None, 0, 8, 128, None) == 0
+    assert kvp.kvp_get_counters()["merge_launches"] == 0

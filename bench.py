@@ -103,6 +103,7 @@ class DecodeBench:
                                   slots=slots, bt=rows.copy(), q=self.q[0].cpu().numpy().view(np.uint16))
             del k, v
         self.out = torch.zeros(self.B, self.Hq, self.D, dtype=torch.int16, device="cuda")
+        self.lse = torch.zeros(self.B, self.Hq, dtype=torch.float32, device="cuda")
         self.ws = kvp.alloc_workspace(self.pool, self.Hq, self.B, self.L)
         self.scale = 1.0 / math.sqrt(self.D)
         self.i = 0
@@ -128,6 +129,42 @@ class DecodeBench:
         self.kvp.kvp_decode_step(self.pool, self.knew[s], self.vnew[s], self.slot_new[s], self.q[s], self.out,
                                  self.Hq, self.bt[s], self.sl, self.qsl, 1, self.L, self.scale, True,
                                  workspace=self.ws)
+
+    def capture_graphs(self):
+        """One HIP graph per page set holding that set's decode step (replayed in rotation)."""
+        import torch
+        self.graphs = []
+        for s in range(self.S):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.kvp.kvp_decode_step(self.pool, self.knew[s], self.vnew[s], self.slot_new[s], self.q[s],
+                                         self.out, self.Hq, self.bt[s], self.sl, self.qsl, 1, self.L, self.scale,
+                                         True, workspace=self.ws)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def capture_chain(self):
+        """One HIP graph holding the decode steps of all S page sets in order:
+        one replay runs S steps with no host work between them."""
+        import torch
+        self.chain = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.chain):
+            for s in range(self.S):
+                self.kvp.kvp_decode_step(self.pool, self.knew[s], self.vnew[s], self.slot_new[s], self.q[s],
+                                         self.out, self.Hq, self.bt[s], self.sl, self.qsl, 1, self.L, self.scale,
+                                         True, workspace=self.ws)
+        torch.cuda.synchronize()
+
+    def graph_step(self):
+        s = self.i % self.S
+        self.i += 1
+        self.graphs[s].replay()
+
+    def attention_lse(self):
+        s = self.i % self.S
+        self.i += 1
+        self.kvp.paged_attention_lse(self.pool, self.q[s], self.out, self.lse, self.Hq, self.bt[s], self.sl,
+                                     self.qsl, 1, self.L, self.scale, True, workspace=self.ws)
 
     def attention_only(self):
         s = self.i % self.S
@@ -165,6 +202,36 @@ class DecodeBench:
                 "kind": "oracle",
                 "sample": "%d full decode calls (B4 KV7168, all 8 heads) in %.1f s, %.1f ms/call; the oracle "
                           "parallelises over query rows, so %d threads were busy" % (n, n * dt, dt * 1e3, threads)}
+
+
+class MergeBench:
+    """kvp_merge_attention over [T=4096, H=32, D=128]: read two BF16 results and their
+    FP32 lse, write the merged result and lse (HBM-bound).  Calls rotate over 4
+    buffer sets (400 MB, above the 256 MB Infinity Cache), so inputs come from HBM."""
+    T, H, D = 4096, 32, 128
+    bytes = 3 * T * H * D * 2 + 3 * T * H * 4
+    SETS = 4
+
+    def __init__(self, seed=1237):
+        import torch
+        import paged_kv_cache_bf16_amd as kvp
+        self.kvp = kvp
+        gen = torch.Generator(device="cuda").manual_seed(seed)
+        shp = (self.T, self.H, self.D)
+        self.sets = []
+        for _ in range(self.SETS):
+            a = torch.randn(shp, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+            b = torch.randn(shp, generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+            la = torch.randn(self.T, self.H, generator=gen, device="cuda") * 4
+            lb = torch.randn(self.T, self.H, generator=gen, device="cuda") * 4
+            self.sets.append((a, la, b, lb, torch.empty_like(a), torch.empty_like(la)))
+        self.i = 0
+        torch.cuda.synchronize()
+
+    def merge(self):
+        a, la, b, lb, out, lse = self.sets[self.i % self.SETS]
+        self.i += 1
+        self.kvp.kvp_merge_attention(a, la, b, lb, out, lse)
 
 
 class PrefillBench:
@@ -304,6 +371,26 @@ def main():
     c0 = kvp.kvp_get_counters()
     assert c0["split_kv_launches"] > 0
 
+    # the same decode step replayed from HIP graphs (one per page set)
+    dec.capture_graphs()
+    for _ in range(args.warmup):
+        dec.graph_step()
+    g_us = time_launches(dec.graph_step, args.steps, stream)
+    log("decode step from graphs: %.2f us/step" % g_us)
+    dec.capture_chain()
+    dec.chain.replay()
+    reps = max(1, args.steps // dec.S)
+    chain_us = time_launches(dec.chain.replay, reps, stream) / dec.S
+    log("decode step from a %d-step graph: %.2f us/step" % (dec.S, chain_us))
+    lse_us = float(np.median([time_launches(dec.attention_lse, 200, stream) for _ in range(5)]))
+    log("decode attention with lse: %.2f us/call" % lse_us)
+
+    # merge of two results over disjoint key sets at the prefill shape (4096 tokens x 32 heads x 128)
+    mg = MergeBench()
+    m_us = float(np.median([time_launches(mg.merge, 50, stream) for _ in range(5)]))
+    log("merge: %.2f us/call, %.0f GB/s" % (m_us, mg.bytes / (m_us * 1e-6) / 1e9))
+    del mg
+
     result = {
         "metric": METRIC,
         "value": round(dec.algo_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -330,6 +417,17 @@ def main():
                      "kernel": "split_partial_kernel<128> + split_fold_kernel<128> (one paged_attention call)",
                      "us_per_call": round(attn_us, 3),
                      "algo_bytes_per_call": dec.algo_bytes},
+        "decode_graph": {"us_per_step": round(g_us, 3), "GBps": round(dec.algo_bytes / (g_us * 1e-6) / 1e9, 2),
+                         "note": "the same step replayed from one captured HIP graph per page set"},
+        "decode_graph_chain": {"us_per_step": round(chain_us, 3),
+                               "GBps": round(dec.algo_bytes / (chain_us * 1e-6) / 1e9, 2),
+                               "note": "the %d page sets' steps captured in order in one graph; no host work "
+                                       "between steps" % dec.S},
+        "decode_lse": {"us_per_call": round(lse_us, 3), "note": "paged_attention_lse on the decode workload"},
+        "merge": {"workload": "kvp_merge_attention of two [4096, 32, 128] BF16 results with FP32 lse",
+                  "us_per_call": round(m_us, 3), "bytes_per_call": MergeBench.bytes,
+                  "GBps": round(MergeBench.bytes / (m_us * 1e-6) / 1e9, 1),
+                  "frac": round(MergeBench.bytes / (m_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "decode_warm_cache": {"us_per_call": round(warm_us, 3),
                               "GBps": round(dec.algo_bytes / (warm_us * 1e-6) / 1e9, 1)},
         "parity": {"decode_max_abs": mx, "decode_mean_abs": mean},

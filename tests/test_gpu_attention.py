@@ -11,8 +11,8 @@ import torch
 
 import paged_kv_cache_bf16_amd as kvp
 from paged_kv_cache_bf16_amd import workloads as wl
-from harness import (GpuCase, bitwise, bf16_to_f32, compare, oracle_attention, oracle_pool,
-                     sample_rows)
+from harness import (GpuCase, bitwise, bf16_to_f32, compare, dev_bits, host_bits, oracle_attention,
+                     oracle_pool, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -360,3 +360,67 @@ def test_invalid_arguments_rejected_before_launch():
     assert e.value.code == kvp.KVP_ERR_UNSUPPORTED
     after = kvp.kvp_get_counters()
     assert after["split_kv_launches"] == before["split_kv_launches"]
+
+
+def test_fused_qkv_view_strides():
+    """q, k and v as column slices of one fused projection output [T, (Hq + 2 Hkv) * D]
+    ("test(rocm): ReshapeAndCache->PagedAttention composition at real dims", review
+    thread on fused-view strides): the cache write and attention read them through
+    their token strides, and the output lands in a wider buffer; bits equal the
+    contiguous run."""
+    lens = [300, 129]
+    w = wl.random_case(91, lens, lens, 8, 2, 128)
+    print("fused qkv view", flush=True)
+    Hq, Hkv, D = 8, 2, 128
+    T = int(w.q.shape[0])
+    assert T == int(w.k.shape[0])           # full prefill: one new token per query
+    Wd = (Hq + 2 * Hkv) * D
+    fused = torch.empty((T, Wd), dtype=torch.int16, device="cuda")
+    fused[:, :Hq * D] = dev_bits(w.q).reshape(T, -1)
+    fused[:, Hq * D:(Hq + Hkv) * D] = dev_bits(w.k).reshape(T, -1)
+    fused[:, (Hq + Hkv) * D:] = dev_bits(w.v).reshape(T, -1)
+    qv = fused[:, :Hq * D].unflatten(1, (Hq, D))
+    kv = fused[:, Hq * D:(Hq + Hkv) * D].unflatten(1, (Hkv, D))
+    vv = fused[:, (Hq + Hkv) * D:].unflatten(1, (Hkv, D))
+    assert qv.stride(0) == Wd and kv.stride(0) == Wd
+    pool = kvp.alloc_pool(w.num_blocks, Hkv, D, fill_bits=0x7FC1)
+    kvp.reshape_and_cache(pool, kv, vv, torch.from_numpy(w.slot_mapping).cuda())
+    bt = torch.from_numpy(kvp.kv_prepare_block_tables(pool, w.block_tables, w.seq_lens)).cuda()
+    sl = torch.from_numpy(w.seq_lens).cuda()
+    qsl = torch.from_numpy(w.query_start_loc).cuda()
+    wide = torch.full((T, Hq * D + 64), -1, dtype=torch.int16, device="cuda")
+    outv = wide[:, :Hq * D].unflatten(1, (Hq, D))
+    kvp.paged_attention(pool, qv, outv, Hq, bt, sl, qsl, int(max(lens)), int(max(lens)), w.scale, True)
+    torch.cuda.synchronize()
+    g = GpuCase(w)
+    ref = g.run()
+    bitwise(host_bits(outv.contiguous()), ref, "fused-view prefill")
+    assert (host_bits(wide[:, Hq * D:]) == 0xFFFF).all(), "wrote past the output rows"
+    np.testing.assert_array_equal(host_bits(pool.storage), g.pool_bits())
+
+
+def test_fused_qkv_view_decode_step():
+    """kvp_decode_step (one launch) reading q, k and v as slices of a fused
+    [B, (Hq + 2 Hkv) * D] projection: same output and pool bits as contiguous
+    inputs."""
+    lens = [700, 129, 2000]
+    Hq, Hkv, D = 8, 2, 128
+    w, slots, kn, vn = _decode_step_case(93, lens, Hq, Hkv, D, [699, 128, 1999])
+    print("fused qkv view decode step", flush=True)
+    out_c, pool_c, delta = _run_step(w, slots, kn, vn, fused=True)
+    assert delta["fused_decode_steps"] == 1
+    B = len(lens)
+    Wd = (Hq + 2 * Hkv) * D
+    fused = torch.empty((B, Wd), dtype=torch.int16, device="cuda")
+    fused[:, :Hq * D] = dev_bits(w.q).reshape(B, -1)
+    fused[:, Hq * D:(Hq + Hkv) * D] = dev_bits(kn).reshape(B, -1)
+    fused[:, (Hq + Hkv) * D:] = dev_bits(vn).reshape(B, -1)
+    g = GpuCase(w)
+    out = torch.full((B, Hq, D), -1, dtype=torch.int16, device="cuda")
+    kvp.kvp_decode_step(g.pool, fused[:, Hq * D:(Hq + Hkv) * D].unflatten(1, (Hkv, D)),
+                        fused[:, (Hq + Hkv) * D:].unflatten(1, (Hkv, D)), torch.from_numpy(slots).cuda(),
+                        fused[:, :Hq * D].unflatten(1, (Hq, D)), out, Hq, g.bt, g.seq_lens, g.qsl, 1,
+                        int(max(lens)), w.scale, True, workspace=g.ws)
+    torch.cuda.synchronize()
+    bitwise(host_bits(out), out_c, "fused-view decode step output")
+    np.testing.assert_array_equal(g.pool_bits(), pool_c)

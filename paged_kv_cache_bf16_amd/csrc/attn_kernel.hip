@@ -1421,6 +1421,483 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     }
 }
 
+// ---------------------------------------------------------------- wave-pair prefill
+
+// Two waves share each 16-column block: wave half h of the pair computes S
+// for key blocks [h NKB/2, (h+1) NKB/2) of the tile and P.V for dim blocks
+// [h NDB/2, (h+1) NDB/2) of the output; the tile max, the per-lane partial
+// sums and P^T go through LDS.  Per column the arithmetic is the tile step of
+// the other kernels: the max is exact in any order; the partial sums are the
+// two halves of the same fixed tree (blocks of half 0, then of half 1, then
+// lanes xor 16 and xor 32); P^T and the fold are unchanged.  Used where one
+// wave per column block would leave CUs idle (few columns per kv head) or
+// would not hold its state in registers (head_dim 512).
+
+template <int D>
+struct HalfState {
+    float R, L;
+    f32x4 acc[Geo<D>::NDB / 2];
+};
+
+// Exchange area of one pair.
+template <int D>
+struct PairX {
+    float mx[2][16];
+    float sum[2][64];
+    bf16x8 p[Geo<D>::NKS][64];
+};
+
+template <int D>
+__device__ __forceinline__ void ws_qk(const char *kl, const Cols<D> &cols, f32x4 (&s)[Geo<D>::NKB / 2], int h)
+{
+    using G = Geo<D>;
+    constexpr int HK = G::NKB / 2;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    const char *base[HK];
+#pragma unroll
+    for (int k = 0; k < HK; ++k) {
+        const int kb = h * HK + k;
+        const int stp = kb >> 1, e = kb & 1;
+        const int page = 2 * stp + (c >> 3);
+        const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
+        base[k] = kl + page * G::PAGE + ksw(tok, page) * 16 + g * 256;
+    }
+    bf16x8 kf[HK], kn[HK];
+#pragma unroll
+    for (int k = 0; k < HK; ++k) {
+        kf[k] = *reinterpret_cast<const bf16x8 *>(base[k]);
+        s[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ds = 0; ds < G::NDS; ++ds) {
+        if (ds + 1 < G::NDS) {
+#pragma unroll
+            for (int k = 0; k < HK; ++k)
+                kn[k] = *reinterpret_cast<const bf16x8 *>(base[k] + (ds + 1) * 1024);
+        }
+#pragma unroll
+        for (int k = 0; k < HK; ++k)
+            s[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], cols.qf[ds], s[k], 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < HK; ++k)
+            kf[k] = kn[k];
+        if (ds + 1 < G::NDS)
+            __builtin_amdgcn_sched_group_barrier(0x100, HK, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, HK, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Stage 1: mask, this half's max of raw scores (exact), to the pair's area.
+template <int D, bool MASK>
+__device__ __forceinline__ void ws_max(f32x4 (&s)[Geo<D>::NKB / 2], int lim, int tile, int h, PairX<D> &x)
+{
+    using G = Geo<D>;
+    constexpr int HK = G::NKB / 2;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    float mk[HK];
+#pragma unroll
+    for (int k = 0; k < HK; ++k) {
+        if (MASK) {
+            const int kb = h * HK + k;
+            const int stp = kb >> 1, e = kb & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = tile * G::T + 32 * stp + 8 * g + 4 * e + i;
+                s[k][i] = key < lim ? s[k][i] : -INFINITY;
+            }
+        }
+        mk[k] = fmax2(fmax2(s[k][0], s[k][1]), fmax2(s[k][2], s[k][3]));
+    }
+#pragma unroll
+    for (int w = 1; w < HK; w *= 2)
+#pragma unroll
+        for (int k = 0; k < HK; k += 2 * w)
+            mk[k] = fmax2(mk[k], mk[k + w]);
+    const float m = max_xor32(max_xor16(mk[0]));
+    if (g == 0)
+        x.mx[h][c] = m;
+}
+
+// Stage 2: the tile max, p, this half's level of the sum tree and its P^T
+// steps to the pair's area.  Returns m (scaled).
+template <int D>
+__device__ __forceinline__ float ws_exp(f32x4 (&s)[Geo<D>::NKB / 2], float scale_log2, int h, PairX<D> &x)
+{
+    using G = Geo<D>;
+    constexpr int HK = G::NKB / 2;
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15;
+    const float m = __fmul_rn(fmax2(x.mx[0][c], x.mx[1][c]), scale_log2);
+    const float nmu = m == -INFINITY ? 0.f : -m;
+    float part[HK];
+#pragma unroll
+    for (int k = 0; k < HK; ++k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s[k][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k][i], scale_log2, nmu));
+        part[k] = __fadd_rn(__fadd_rn(s[k][0], s[k][1]), __fadd_rn(s[k][2], s[k][3]));
+    }
+#pragma unroll
+    for (int w = 1; w < HK; w *= 2)
+#pragma unroll
+        for (int k = 0; k < HK; k += 2 * w)
+            part[k] = __fadd_rn(part[k], part[k + w]);
+    x.sum[h][lane] = part[0];
+#pragma unroll
+    for (int sl = 0; sl < HK / 2; ++sl) {
+        bf16x8 pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = (__bf16)s[2 * sl][i];
+            pv[4 + i] = (__bf16)s[2 * sl + 1][i];
+        }
+        x.p[h * (HK / 2) + sl][lane] = pv;
+    }
+    return m;
+}
+
+// Stage 3: l (the tree's last levels), the fold of (R, L), the rescale of
+// this half's ACC if some reference moved, then P.V for this half's dims
+// folded with fma(tile, h, ACC).
+template <int D, int DG>
+__device__ __forceinline__ void ws_fold_pv(const char *vl, float m, int h, const PairX<D> &x, HalfState<D> &st)
+{
+    using G = Geo<D>;
+    constexpr int HD = G::NDB / 2;
+    static_assert(HD % DG == 0, "whole groups");
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    float l = __fadd_rn(x.sum[0][lane], x.sum[1][lane]);
+    l = sum_xor32(sum_xor16(l));
+    bf16x8 pf[G::NKS];
+#pragma unroll
+    for (int stp = 0; stp < G::NKS; ++stp)
+        pf[stp] = x.p[stp][lane];
+    const FoldF f = fold_factors(st.R, m);
+    const bool any_up = __ballot(f.up) != 0;
+    st.L = fold1v(st.L, l, f.gs, f.h);
+    st.R = f.Rn;
+    if (any_up) {
+#pragma unroll
+        for (int db = 0; db < HD; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                st.acc[db][i] = __fmul_rn(st.acc[db][i], f.gs);
+    }
+    auto vaddr = [&](int db, int stp) -> const char * {
+        const int d = 16 * db + c;
+        return vl + (g >> 1) * G::PAGE + (d * 2 + vsw(g & 1, d)) * 16 + 2 * stp * G::PAGE;
+    };
+#pragma unroll
+    for (int d0 = 0; d0 < HD; d0 += DG) {
+        f32x4 o[DG];
+        bf16x8 vf[DG], vn[DG];
+#pragma unroll
+        for (int d = 0; d < DG; ++d) {
+            o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+            vf[d] = *reinterpret_cast<const bf16x8 *>(vaddr(h * HD + d0 + d, 0));
+        }
+#pragma unroll
+        for (int stp = 0; stp < G::NKS; ++stp) {
+            if (stp + 1 < G::NKS) {
+#pragma unroll
+                for (int d = 0; d < DG; ++d)
+                    vn[d] = *reinterpret_cast<const bf16x8 *>(vaddr(h * HD + d0 + d, stp + 1));
+            }
+#pragma unroll
+            for (int d = 0; d < DG; ++d)
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], pf[stp], o[d], 0, 0, 0);
+#pragma unroll
+            for (int d = 0; d < DG; ++d)
+                vf[d] = vn[d];
+            if (stp + 1 < G::NKS)
+                __builtin_amdgcn_sched_group_barrier(0x100, DG, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, DG, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int d = 0; d < DG; ++d)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                st.acc[d0 + d][i] = __builtin_fmaf(o[d][i], f.h, st.acc[d0 + d][i]);
+    }
+}
+
+// This half's dims of the column's output (and its lse from half 0).
+template <int D>
+__device__ __forceinline__ void ws_store(const AttnArgs &a, const ColInfo &ci, const HalfState<D> &st, int h)
+{
+    constexpr int HD = Geo<D>::NDB / 2;
+    const int g = (threadIdx.x & 63) >> 4;
+    if (a.lse && h == 0 && g == 0)
+        a.lse[ci.row * a.lse_token_stride + ci.head] = lse_of(st.R, st.L);
+    const float inv = 1.0f / st.L;
+    uint16_t *dst = a.out + ci.row * a.out_token_stride + (int64_t)ci.head * D + 4 * g + 16 * h * HD;
+#pragma unroll
+    for (int db = 0; db < HD; ++db)
+        *reinterpret_cast<u32x2 *>(dst + 16 * db) = finish4(st.acc[db], inv);
+}
+
+// Shared set-up of the wave-pair kernels: workgroup -> (column group, kv
+// head, sequence) as in the other prefill kernels; wave w -> pair w / 2,
+// half w % 2.
+struct WsSetup {
+    int b, kvh, cg, q0, q_len, seq_len, ncols, last, wave, pair, half;
+    bool run;
+};
+
+template <int D, int NWV>
+__device__ __forceinline__ WsSetup ws_setup(const AttnArgs &a)
+{
+    constexpr int NCOL = NWV / 2 * 16;
+    WsSetup w{};
+    w.run = false;
+    const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
+    const int per = (n + 7) / 8;
+    const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (j >= n)
+        return w;
+    const int cgi = j % a.col_groups;
+    w.kvh = (j / a.col_groups) % a.num_kv_heads;
+    w.b = j / (a.col_groups * a.num_kv_heads);
+    w.cg = a.col_groups - 1 - cgi;                  // heaviest (latest) columns first
+    if (!row_ok(a, w.b, w.q0, w.q_len, w.seq_len))
+        return w;
+    w.ncols = w.q_len * a.group;
+    if (w.cg * NCOL >= w.ncols || w.ncols <= a.split_cols)
+        return w;
+    const int col_last = min((w.cg + 1) * NCOL, w.ncols) - 1;
+    const int pos_last = w.seq_len - w.q_len + col_last / a.group;
+    w.last = (a.causal ? pos_last : w.seq_len - 1) / Geo<D>::T;
+    w.wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    w.pair = w.wave >> 1;
+    w.half = w.wave & 1;
+    w.run = true;
+    return w;
+}
+
+// Double-buffered wave-pair kernel (head_dim 128 and 256): the K+V tile
+// staging of prefill_db_kernel, three barriers per tile (halves' maxima,
+// then partial sums and P^T, then the buffer swap).
+template <int D, int NWV, int WPE>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void prefill_ws_db_kernel(AttnArgs a)
+{
+    using G = Geo<D>;
+    constexpr int NCOL = NWV / 2 * 16;
+    constexpr int HALF = G::NKB * G::PAGE;
+    constexpr int CPP = G::PAGE / 1024;
+    constexpr int CPW = G::NKB * CPP / NWV;
+    static_assert(CPW >= 1 && (G::NKB * CPP) % NWV == 0, "whole chunks per wave");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    int32_t *const ids = reinterpret_cast<int32_t *>(lds + 4 * HALF);                 // [2][NKB]
+    PairX<D> *const xs = reinterpret_cast<PairX<D> *>(lds + 4 * HALF + 2 * G::NKB * 4);   // [NWV / 2]
+
+    const WsSetup w = ws_setup<D, NWV>(a);
+    if (!w.run)
+        return;
+    const int c = threadIdx.x & 15;
+    const int32_t *bt_row = a.block_tables + (int64_t)w.b * a.bt_stride;
+    Cols<D> cols;
+    HalfState<D> st;
+    const int col = w.cg * NCOL + w.pair * 16 + c;
+    const ColInfo ci = col_info(a, col, w.kvh, w.q0, w.q_len, w.seq_len);
+    load_q<D>(cols, a, ci);
+    st.R = -INFINITY;
+    st.L = 0.f;
+#pragma unroll
+    for (int db = 0; db < G::NDB / 2; ++db)
+        st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool active = w.cg * NCOL + w.pair * 16 < w.ncols;
+    int min_lim = cols.lim;
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2)
+        min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
+    PairX<D> &x = xs[w.pair];
+
+    auto lds_addr = [](const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p; };
+    auto kbuf = [&](int tile) { return lds + (tile & 1) * 2 * HALF; };
+    auto issue = [&](int tile) {
+        char *const buf = kbuf(tile);
+        const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int ch = w.wave * CPW + i;
+            const int page = ch / CPP, part = ch % CPP;
+            int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
+            id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
+            const int64_t hoff = (int64_t)w.kvh * BS * D;
+            const char *ks = reinterpret_cast<const char *>(a.k_cache + (int64_t)id * a.k_block_stride + hoff);
+            const char *vs = reinterpret_cast<const char *>(a.v_cache + (int64_t)id * a.v_block_stride + hoff);
+            const DbOffsets o = db_offsets(page);
+            db_chunk(ks + part * 1024, o.k, lds_addr(buf + page * G::PAGE + part * 1024));
+            db_chunk(vs + part * 1024, o.v, lds_addr(buf + HALF + page * G::PAGE + part * 1024));
+        }
+    };
+    auto fetch_ids = [&](int tile) {
+        if (w.wave == 0)
+            id_dma(bt_row + tile * G::NKB, G::NKB, lds_addr(ids + (tile & 1) * G::NKB));
+    };
+
+    fetch_ids(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    issue(0);
+    if (w.last >= 1)
+        fetch_ids(1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int t = 0; t <= w.last; ++t) {
+        if (t < w.last) {
+            issue(t + 1);
+            if (t + 2 <= w.last)
+                fetch_ids(t + 2);
+        }
+        char *const cur = kbuf(t);
+        if ((t + 1) * G::T > w.seq_len) {
+            db_mask_tail<D, NWV>(cur + HALF, w.seq_len, t);
+            __syncthreads();
+        }
+        f32x4 s[G::NKB / 2];
+        float m = 0.f;
+        if (active) {
+            ws_qk<D>(cur, cols, s, w.half);
+            if ((t + 1) * G::T > min_lim)
+                ws_max<D, true>(s, cols.lim, t, w.half, x);
+            else
+                ws_max<D, false>(s, cols.lim, t, w.half, x);
+        }
+        __syncthreads();
+        if (active)
+            m = ws_exp<D>(s, a.scale_log2, w.half, x);
+        __syncthreads();
+        if (active)
+            ws_fold_pv<D, (D == 128 ? 4 : 4)>(cur + HALF, m, w.half, x, st);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    if (ci.lim > 0)
+        ws_store<D>(a, ci, st, w.half);
+}
+
+// Single-buffered wave-pair kernel (head_dim 512, whose K+V tile takes 128
+// KB of LDS): the staging order of prefill_sb_kernel; the pair exchanges
+// share its barriers (the maxima with "K(t) read", P^T and the sums with
+// "V(t) landed").
+template <int D, int NWV, int WPE>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void prefill_ws_sb_kernel(AttnArgs a)
+{
+    using G = Geo<D>;
+    constexpr int NCOL = NWV / 2 * 16;
+    constexpr int HALF = G::NKB * G::PAGE;
+    constexpr int CPP = G::PAGE / 1024;
+    constexpr int CPW = G::NKB * CPP / NWV;
+    static_assert(CPW >= 1 && (G::NKB * CPP) % NWV == 0, "whole chunks per wave");
+    static_assert(CPW + 1 < 64, "vmcnt range");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    char *const kbuf = lds;
+    char *const vbuf = lds + HALF;
+    int32_t *const ids = reinterpret_cast<int32_t *>(lds + 2 * HALF);                 // [2][NKB]
+    PairX<D> *const xs = reinterpret_cast<PairX<D> *>(lds + 2 * HALF + 2 * G::NKB * 4);   // [NWV / 2]
+
+    const WsSetup w = ws_setup<D, NWV>(a);
+    if (!w.run)
+        return;
+    const int c = threadIdx.x & 15;
+    const int32_t *bt_row = a.block_tables + (int64_t)w.b * a.bt_stride;
+    Cols<D> cols;
+    HalfState<D> st;
+    const int col = w.cg * NCOL + w.pair * 16 + c;
+    const ColInfo ci = col_info(a, col, w.kvh, w.q0, w.q_len, w.seq_len);
+    load_q<D>(cols, a, ci);
+    st.R = -INFINITY;
+    st.L = 0.f;
+#pragma unroll
+    for (int db = 0; db < G::NDB / 2; ++db)
+        st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool active = w.cg * NCOL + w.pair * 16 < w.ncols;
+    int min_lim = cols.lim;
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2)
+        min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
+    PairX<D> &x = xs[w.pair];
+
+    auto lds_addr = [](const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p; };
+    auto issue = [&](bool is_k, int tile) {
+        char *const buf = is_k ? kbuf : vbuf;
+        const uint16_t *const cache = is_k ? a.k_cache : a.v_cache;
+        const int64_t stride = is_k ? a.k_block_stride : a.v_block_stride;
+        const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int ch = w.wave * CPW + i;
+            const int page = ch / CPP, part = ch % CPP;
+            int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
+            id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
+            const char *src = reinterpret_cast<const char *>(cache + (int64_t)id * stride + (int64_t)w.kvh * BS * D);
+            const DbOffsets o = db_offsets(page);
+            db_chunk(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
+        }
+    };
+    auto fetch_ids = [&](int tile) {
+        if (w.wave == 0)
+            id_dma(bt_row + tile * G::NKB, G::NKB, lds_addr(ids + (tile & 1) * G::NKB));
+    };
+
+    fetch_ids(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    issue(true, 0);
+    issue(false, 0);
+    if (w.last >= 1)
+        fetch_ids(1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int t = 0; t <= w.last; ++t) {
+        f32x4 s[G::NKB / 2];
+        float m = 0.f;
+        if (active) {
+            ws_qk<D>(kbuf, cols, s, w.half);
+            if ((t + 1) * G::T > min_lim)
+                ws_max<D, true>(s, cols.lim, t, w.half, x);
+            else
+                ws_max<D, false>(s, cols.lim, t, w.half, x);
+        }
+        __syncthreads();                                   // K(t) read by every wave; maxima visible
+        if (t < w.last)
+            issue(true, t + 1);
+        if (active)
+            m = ws_exp<D>(s, a.scale_log2, w.half, x);
+        // V(t) (issued before K(t+1)) has landed
+        if (t < w.last)
+            wait_vm<CPW>();
+        else
+            wait_vm<0>();
+        __syncthreads();                                   // sums and P^T visible
+        if ((t + 1) * G::T > w.seq_len) {
+            db_mask_tail<D, NWV>(vbuf, w.seq_len, t);
+            __syncthreads();
+        }
+        if (active)
+            ws_fold_pv<D, 4>(vbuf, m, w.half, x, st);
+        __syncthreads();                                   // V(t) read by every wave
+        if (t < w.last) {
+            if (t + 2 <= w.last)
+                fetch_ids(t + 2);
+            issue(false, t + 1);
+            // K(t+1) and the ids of t+2 (issued before V(t+1)) have landed
+            wait_vm<CPW>();
+            __syncthreads();
+        }
+    }
+    if (ci.lim > 0)
+        ws_store<D>(a, ci, st, w.half);
+}
+
 // ---------------------------------------------------------------- ping-pong prefill
 
 // Same column/tile work and per-column arithmetic as prefill_db_kernel, for
@@ -1651,6 +2128,34 @@ static hipError_t prefill_db_launch(AttnArgs a, hipStream_t s, uint64_t *blocks,
     return hipGetLastError();
 }
 
+template <int D, int NWV, int WPE, bool SB>
+static hipError_t prefill_ws_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
+{
+    constexpr int NCOL = NWV / 2 * 16;
+    constexpr int LDS_BYTES = (SB ? 1 : 2) * Geo<D>::LDS + 2 * Geo<D>::NKB * 4 + NWV / 2 * (int)sizeof(PairX<D>);
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
+    const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;
+    const int64_t grid = (n + 7) / 8 * 8;
+    if (grid <= 0)
+        return hipSuccess;
+    if (grid > 0x7fffffff)
+        return hipErrorInvalidValue;
+    if constexpr (SB) {
+        static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_ws_sb_kernel<D, NWV, WPE>,
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        (void)attr;
+        hipLaunchKernelGGL((prefill_ws_sb_kernel<D, NWV, WPE>), dim3((unsigned)grid), dim3(NWV * 64), LDS_BYTES, s, a);
+    } else {
+        static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_ws_db_kernel<D, NWV, WPE>,
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        (void)attr;
+        hipLaunchKernelGGL((prefill_ws_db_kernel<D, NWV, WPE>), dim3((unsigned)grid), dim3(NWV * 64), LDS_BYTES, s, a);
+    }
+    *blocks = (uint64_t)grid;
+    return hipGetLastError();
+}
+
 template <int D, int CB>
 static hipError_t prefill_pp_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
 {
@@ -1675,16 +2180,29 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
     const int mq = max_query_len;
     // Dh 128: the ping-pong kernel (256 columns per workgroup) when it still
     // yields a workgroup per CU (256 CUs), else the double-buffered kernel
-    // with 128 columns.  Dh 256: double-buffered.  Dh 512: one K and one V
-    // buffer (a double-buffered tile would not fit in LDS).
-    const int64_t db_groups = (int64_t)a.num_seqs * a.num_kv_heads * ((mq * a.group + 255) / 256);
+    // with 128 columns if that does, else the wave-pair kernel (64 columns,
+    // twice the workgroups).  Dh 256: double-buffered or wave-pair by the
+    // same rule.  Dh 512 (one K and one V buffer; a double-buffered tile
+    // would not fit in LDS): 128 columns per workgroup from two workgroups
+    // per CU on (fewer re-reads of the pages), else the wave-pair kernel.
+    const int64_t rows = (int64_t)a.num_seqs * a.num_kv_heads;
+    const int64_t groups256 = rows * ((mq * a.group + 255) / 256);
+    const int64_t groups128 = rows * ((mq * a.group + 127) / 128);
     switch (head_dim) {
     case 128:
-        if (db_groups >= 256)
+        if (groups256 >= 256)
             return prefill_pp_launch<128, 2>(a, s, blocks, mq);
-        return prefill_db_launch<128, 1, 8, 2>(a, s, blocks, mq);
-    case 256: return prefill_db_launch<256, 1, 8, 2>(a, s, blocks, mq);
-    case 512: return prefill_sb_launch<512, 1, 8, 2>(a, s, blocks, mq);
+        if (groups128 >= 256)
+            return prefill_db_launch<128, 1, 8, 2>(a, s, blocks, mq);
+        return prefill_ws_launch<128, 8, 2, false>(a, s, blocks, mq);
+    case 256:
+        if (groups128 >= 256)
+            return prefill_db_launch<256, 1, 8, 2>(a, s, blocks, mq);
+        return prefill_ws_launch<256, 8, 2, false>(a, s, blocks, mq);
+    case 512:
+        if (groups128 >= 512)
+            return prefill_sb_launch<512, 1, 8, 2>(a, s, blocks, mq);
+        return prefill_ws_launch<512, 8, 2, true>(a, s, blocks, mq);
     default: return hipErrorInvalidValue;
     }
 }

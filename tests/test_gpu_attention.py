@@ -424,3 +424,23 @@ def test_fused_qkv_view_decode_step():
     torch.cuda.synchronize()
     bitwise(host_bits(out), out_c, "fused-view decode step output")
     np.testing.assert_array_equal(g.pool_bits(), pool_c)
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,D,ncol", [
+    ([1500], 32, 8, 128, 128),           # 376 workgroups of 128 columns: prefill_db_kernel<128>
+    ([4100, 4100], 8, 2, 256, 128),      # 516 workgroups of 128 columns: prefill_db_kernel<256>
+    ([300, 133], 32, 8, 128, 64),        # few columns: wave-pair kernel, 64 columns per workgroup
+    ([900], 16, 2, 512, 64),             # head_dim 512, small grid: wave-pair kernel
+], ids=["db128", "db256", "ws128", "ws512"])
+def test_prefill_kernel_per_grid_size(lens, Hq, Hkv, D, ncol):
+    """Each prefill kernel the launcher picks by grid size (identified by its
+    workgroup count) against the oracle on sampled rows, and every row's
+    decode against its prefill row bitwise."""
+    w = wl.random_case(97 + D + len(lens), lens, lens, Hq, Hkv, D)
+    G = Hq // Hkv
+    expect = -(-(w.batch * Hkv * (-(-int(w.max_query_len) * G // ncol))) // 8) * 8
+    g, full, _ = _run_and_compare(w, rows=sample_rows(w, 48), what="kernel for %s D=%d" % (lens, D))
+    assert kvp.kvp_get_counters()["last_grid_blocks"] == expect
+    d = w.decode_view()
+    g.set_queries(d.q, d.query_lens)
+    bitwise(g.run(), full[w.query_start_loc[1:] - 1], "decode vs prefill last rows (%s, D=%d)" % (lens, D))

@@ -1429,9 +1429,9 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
 // sums and P^T go through LDS.  Per column the arithmetic is the tile step of
 // the other kernels: the max is exact in any order; the partial sums are the
 // two halves of the same fixed tree (blocks of half 0, then of half 1, then
-// lanes xor 16 and xor 32); P^T and the fold are unchanged.  Used where one
-// wave per column block would leave CUs idle (few columns per kv head) or
-// would not hold its state in registers (head_dim 512).
+// lanes xor 16 and xor 32); P^T and the fold are unchanged.  Used for
+// head_dim 512 grids too small for two 128-column workgroups per CU: half of
+// ACC per wave holds the state in registers without spills.
 
 template <int D>
 struct HalfState {
@@ -1679,110 +1679,6 @@ __device__ __forceinline__ WsSetup ws_setup(const AttnArgs &a)
     return w;
 }
 
-// Double-buffered wave-pair kernel (head_dim 128 and 256): the K+V tile
-// staging of prefill_db_kernel, three barriers per tile (halves' maxima,
-// then partial sums and P^T, then the buffer swap).
-template <int D, int NWV, int WPE>
-__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void prefill_ws_db_kernel(AttnArgs a)
-{
-    using G = Geo<D>;
-    constexpr int NCOL = NWV / 2 * 16;
-    constexpr int HALF = G::NKB * G::PAGE;
-    constexpr int CPP = G::PAGE / 1024;
-    constexpr int CPW = G::NKB * CPP / NWV;
-    static_assert(CPW >= 1 && (G::NKB * CPP) % NWV == 0, "whole chunks per wave");
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    int32_t *const ids = reinterpret_cast<int32_t *>(lds + 4 * HALF);                 // [2][NKB]
-    PairX<D> *const xs = reinterpret_cast<PairX<D> *>(lds + 4 * HALF + 2 * G::NKB * 4);   // [NWV / 2]
-
-    const WsSetup w = ws_setup<D, NWV>(a);
-    if (!w.run)
-        return;
-    const int c = threadIdx.x & 15;
-    const int32_t *bt_row = a.block_tables + (int64_t)w.b * a.bt_stride;
-    Cols<D> cols;
-    HalfState<D> st;
-    const int col = w.cg * NCOL + w.pair * 16 + c;
-    const ColInfo ci = col_info(a, col, w.kvh, w.q0, w.q_len, w.seq_len);
-    load_q<D>(cols, a, ci);
-    st.R = -INFINITY;
-    st.L = 0.f;
-#pragma unroll
-    for (int db = 0; db < G::NDB / 2; ++db)
-        st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool active = w.cg * NCOL + w.pair * 16 < w.ncols;
-    int min_lim = cols.lim;
-#pragma unroll
-    for (int off = 1; off < 64; off *= 2)
-        min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
-    PairX<D> &x = xs[w.pair];
-
-    auto lds_addr = [](const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p; };
-    auto kbuf = [&](int tile) { return lds + (tile & 1) * 2 * HALF; };
-    auto issue = [&](int tile) {
-        char *const buf = kbuf(tile);
-        const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            const int ch = w.wave * CPW + i;
-            const int page = ch / CPP, part = ch % CPP;
-            int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
-            id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
-            const int64_t hoff = (int64_t)w.kvh * BS * D;
-            const char *ks = reinterpret_cast<const char *>(a.k_cache + (int64_t)id * a.k_block_stride + hoff);
-            const char *vs = reinterpret_cast<const char *>(a.v_cache + (int64_t)id * a.v_block_stride + hoff);
-            const DbOffsets o = db_offsets(page);
-            db_chunk(ks + part * 1024, o.k, lds_addr(buf + page * G::PAGE + part * 1024));
-            db_chunk(vs + part * 1024, o.v, lds_addr(buf + HALF + page * G::PAGE + part * 1024));
-        }
-    };
-    auto fetch_ids = [&](int tile) {
-        if (w.wave == 0)
-            id_dma(bt_row + tile * G::NKB, G::NKB, lds_addr(ids + (tile & 1) * G::NKB));
-    };
-
-    fetch_ids(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    issue(0);
-    if (w.last >= 1)
-        fetch_ids(1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int t = 0; t <= w.last; ++t) {
-        if (t < w.last) {
-            issue(t + 1);
-            if (t + 2 <= w.last)
-                fetch_ids(t + 2);
-        }
-        char *const cur = kbuf(t);
-        if ((t + 1) * G::T > w.seq_len) {
-            db_mask_tail<D, NWV>(cur + HALF, w.seq_len, t);
-            __syncthreads();
-        }
-        f32x4 s[G::NKB / 2];
-        float m = 0.f;
-        if (active) {
-            ws_qk<D>(cur, cols, s, w.half);
-            if ((t + 1) * G::T > min_lim)
-                ws_max<D, true>(s, cols.lim, t, w.half, x);
-            else
-                ws_max<D, false>(s, cols.lim, t, w.half, x);
-        }
-        __syncthreads();
-        if (active)
-            m = ws_exp<D>(s, a.scale_log2, w.half, x);
-        __syncthreads();
-        if (active)
-            ws_fold_pv<D, (D == 128 ? 4 : 4)>(cur + HALF, m, w.half, x, st);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
-    if (ci.lim > 0)
-        ws_store<D>(a, ci, st, w.half);
-}
-
 // Single-buffered wave-pair kernel (head_dim 512, whose K+V tile takes 128
 // KB of LDS): the staging order of prefill_sb_kernel; the pair exchanges
 // share its barriers (the maxima with "K(t) read", P^T and the sums with
@@ -1896,6 +1792,176 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     }
     if (ci.lim > 0)
         ws_store<D>(a, ci, st, w.half);
+}
+
+// ---------------------------------------------------------------- producer / consumer prefill
+
+// Two waves per 16-column block split the tile step by stage instead of by
+// keys: the producer (waves 0-3) runs QK and the softmax statistics of tile
+// t, folds (R, L) and hands the fold factors and P^T to its consumer (waves
+// 4-7) through LDS; the consumer runs P.V of tile t-1 and folds it into ACC
+// at the same time.  Both roles use the tile-step functions of the other
+// kernels unchanged, so the bits are the same; the two waves of a SIMD are a
+// stage apart, so one's MFMAs fill the other's softmax.  K and V tiles have
+// two LDS buffers each (K(t+1) and V(t) load while K(t) and V(t-1) are read),
+// two barriers per tile.  64 columns per workgroup, for grids that leave
+// CUs idle with more columns per workgroup.
+template <int D>
+struct StageX {
+    bf16x8 p[Geo<D>::NKS][64];
+    float gs[64], h[64], R[64], L[64];
+    int up;
+};
+
+template <int D, int WPE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void prefill_ss_kernel(AttnArgs a)
+{
+    using G = Geo<D>;
+    constexpr int NWV = 8;
+    constexpr int NCOL = 64;
+    constexpr int HALF = G::NKB * G::PAGE;
+    constexpr int CPP = G::PAGE / 1024;
+    constexpr int CPW = G::NKB * CPP / NWV;          // K (or V) chunks per wave per tile
+    static_assert(CPW >= 1 && (G::NKB * CPP) % NWV == 0, "whole chunks per wave");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    int32_t *const ids = reinterpret_cast<int32_t *>(lds + 4 * HALF);                   // [2][NKB]
+    StageX<D> *const xs = reinterpret_cast<StageX<D> *>(lds + 4 * HALF + 2 * G::NKB * 4);   // [4]
+
+    const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
+    const int per = (n + 7) / 8;
+    const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (j >= n)
+        return;
+    const int cgi = j % a.col_groups;
+    const int kvh = (j / a.col_groups) % a.num_kv_heads;
+    const int b = j / (a.col_groups * a.num_kv_heads);
+    const int cg = a.col_groups - 1 - cgi;           // heaviest (latest) columns first
+    int q0, q_len, seq_len;
+    if (!row_ok(a, b, q0, q_len, seq_len))
+        return;
+    const int ncols = q_len * a.group;
+    if (cg * NCOL >= ncols || ncols <= a.split_cols)
+        return;
+    const int col_last = min((cg + 1) * NCOL, ncols) - 1;
+    const int pos_last = seq_len - q_len + col_last / a.group;
+    const int last = (a.causal ? pos_last : seq_len - 1) / G::T;
+    const int32_t *bt_row = a.block_tables + (int64_t)b * a.bt_stride;
+
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int blk = wave & 3;                  // column block
+    const bool producer = wave < 4;
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15;
+    StageX<D> &x = xs[blk];
+    const int col = cg * NCOL + blk * 16 + c;
+    const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
+    const bool active = cg * NCOL + blk * 16 < ncols;
+    Cols<D> cols[1];
+    State<D> st[1];
+    int min_lim = 0;
+    if (producer) {
+        load_q<D>(cols[0], a, ci);
+        min_lim = cols[0].lim;
+#pragma unroll
+        for (int off = 1; off < 64; off *= 2)
+            min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
+    }
+    state_init<D>(st[0]);
+
+    auto lds_addr = [](const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p; };
+    auto stage = [&](int tile) { return lds + (tile & 1) * 2 * HALF; };
+    // this wave's chunks of the K (or V) part of `tile`
+    auto issue = [&](bool is_k, int tile) {
+        char *const buf = stage(tile) + (is_k ? 0 : HALF);
+        const uint16_t *const cache = is_k ? a.k_cache : a.v_cache;
+        const int64_t stride = is_k ? a.k_block_stride : a.v_block_stride;
+        const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int ch = wave * CPW + i;
+            const int page = ch / CPP, part = ch % CPP;
+            int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
+            id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
+            const char *src = reinterpret_cast<const char *>(cache + (int64_t)id * stride + (int64_t)kvh * BS * D);
+            const DbOffsets o = db_offsets(page);
+            db_chunk(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
+        }
+    };
+    auto fetch_ids = [&](int tile) {
+        if (wave == 0)
+            id_dma(bt_row + tile * G::NKB, G::NKB, lds_addr(ids + (tile & 1) * G::NKB));
+    };
+
+    // ---- prologue: ids of tiles 0 and 1, then K(0)
+    fetch_ids(0);
+    if (last >= 1)
+        fetch_ids(1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    issue(true, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // step t: the producer computes tile t, the consumer tile t - 1
+    for (int t = 0; t <= last + 1; ++t) {
+        // K(t+1) and V(t) go into buffers last read in step t - 1
+        if (t + 1 <= last)
+            issue(true, t + 1);
+        if (t <= last)
+            issue(false, t);
+        // V(t-1) of a tile that reaches seq_len: zero its keys >= seq_len
+        if (t >= 1 && t * G::T > seq_len) {
+            db_mask_tail<D, NWV>(stage(t - 1) + HALF, seq_len, t - 1);
+            __syncthreads();
+        }
+        bf16x8 pf[1][G::NKS];
+        FoldF f[1];
+        bool any_up = false;
+        if (producer) {
+            if (active && t <= last) {
+                f32x4 sc[1][G::NKB];
+                tile_qk<D, 1>(stage(t), cols, sc);
+                if ((t + 1) * G::T > min_lim)
+                    any_up = prefill_softmax_stats<D, 1, true>(sc, cols, t, a.scale_log2, st, pf, f);
+                else
+                    any_up = prefill_softmax_stats<D, 1, false>(sc, cols, t, a.scale_log2, st, pf, f);
+            }
+        } else if (active && t >= 1) {
+#pragma unroll
+            for (int stp = 0; stp < G::NKS; ++stp)
+                pf[0][stp] = x.p[stp][lane];
+            f[0].gs = x.gs[lane];
+            f[0].h = x.h[lane];
+            if (x.up)
+                rescale_states<D, 1>(st, f);
+            tile_pv<D, 1>(stage(t - 1) + HALF, pf, f, st);
+        }
+        __syncthreads();                                   // the consumer is done with the hand-off of t - 1
+        if (t + 2 <= last)
+            fetch_ids(t + 2);                              // its slot held the ids of V(t), issued above
+        if (producer && active && t <= last) {
+#pragma unroll
+            for (int stp = 0; stp < G::NKS; ++stp)
+                x.p[stp][lane] = pf[0][stp];
+            x.gs[lane] = f[0].gs;
+            x.h[lane] = f[0].h;
+            if (lane == 0)
+                x.up = any_up ? 1 : 0;
+            if (t == last) {
+                x.R[lane] = st[0].R;
+                x.L[lane] = st[0].L;
+            }
+        }
+        if (t <= last) {
+            __builtin_amdgcn_s_waitcnt(0);                 // K(t+1), V(t), ids(t+2) landed
+            __syncthreads();                               // and the hand-off of t is visible
+        }
+    }
+    if (!producer && ci.lim > 0) {
+        st[0].R = x.R[lane];
+        st[0].L = x.L[lane];
+        store_out<D>(a, ci, st[0]);
+    }
 }
 
 // ---------------------------------------------------------------- ping-pong prefill
@@ -2128,11 +2194,11 @@ static hipError_t prefill_db_launch(AttnArgs a, hipStream_t s, uint64_t *blocks,
     return hipGetLastError();
 }
 
-template <int D, int NWV, int WPE, bool SB>
+template <int D, int NWV, int WPE>
 static hipError_t prefill_ws_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
 {
     constexpr int NCOL = NWV / 2 * 16;
-    constexpr int LDS_BYTES = (SB ? 1 : 2) * Geo<D>::LDS + 2 * Geo<D>::NKB * 4 + NWV / 2 * (int)sizeof(PairX<D>);
+    constexpr int LDS_BYTES = Geo<D>::LDS + 2 * Geo<D>::NKB * 4 + NWV / 2 * (int)sizeof(PairX<D>);
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
     const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;
@@ -2141,17 +2207,31 @@ static hipError_t prefill_ws_launch(AttnArgs a, hipStream_t s, uint64_t *blocks,
         return hipSuccess;
     if (grid > 0x7fffffff)
         return hipErrorInvalidValue;
-    if constexpr (SB) {
-        static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_ws_sb_kernel<D, NWV, WPE>,
-                                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        (void)attr;
-        hipLaunchKernelGGL((prefill_ws_sb_kernel<D, NWV, WPE>), dim3((unsigned)grid), dim3(NWV * 64), LDS_BYTES, s, a);
-    } else {
-        static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_ws_db_kernel<D, NWV, WPE>,
-                                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        (void)attr;
-        hipLaunchKernelGGL((prefill_ws_db_kernel<D, NWV, WPE>), dim3((unsigned)grid), dim3(NWV * 64), LDS_BYTES, s, a);
-    }
+    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_ws_sb_kernel<D, NWV, WPE>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    (void)attr;
+    hipLaunchKernelGGL((prefill_ws_sb_kernel<D, NWV, WPE>), dim3((unsigned)grid), dim3(NWV * 64), LDS_BYTES, s, a);
+    *blocks = (uint64_t)grid;
+    return hipGetLastError();
+}
+
+template <int D, int WPE>
+static hipError_t prefill_ss_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
+{
+    constexpr int NCOL = 64;
+    constexpr int LDS_BYTES = 2 * Geo<D>::LDS + 2 * Geo<D>::NKB * 4 + 4 * (int)sizeof(StageX<D>);
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
+    const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;
+    const int64_t grid = (n + 7) / 8 * 8;
+    if (grid <= 0)
+        return hipSuccess;
+    if (grid > 0x7fffffff)
+        return hipErrorInvalidValue;
+    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_ss_kernel<D, WPE>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    (void)attr;
+    hipLaunchKernelGGL((prefill_ss_kernel<D, WPE>), dim3((unsigned)grid), dim3(512), LDS_BYTES, s, a);
     *blocks = (uint64_t)grid;
     return hipGetLastError();
 }
@@ -2180,11 +2260,12 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
     const int mq = max_query_len;
     // Dh 128: the ping-pong kernel (256 columns per workgroup) when it still
     // yields a workgroup per CU (256 CUs), else the double-buffered kernel
-    // with 128 columns if that does, else the wave-pair kernel (64 columns,
-    // twice the workgroups).  Dh 256: double-buffered or wave-pair by the
-    // same rule.  Dh 512 (one K and one V buffer; a double-buffered tile
-    // would not fit in LDS): 128 columns per workgroup from two workgroups
-    // per CU on (fewer re-reads of the pages), else the wave-pair kernel.
+    // with 128 columns if that does, else the producer / consumer kernel (64
+    // columns, twice the workgroups).  Dh 256: double-buffered or producer /
+    // consumer by the same rule.  Dh 512 (one K and one V buffer; a
+    // double-buffered tile would not fit in LDS): 128 columns per workgroup
+    // from two workgroups per CU on (fewer re-reads of the pages), else the
+    // wave-pair kernel.
     const int64_t rows = (int64_t)a.num_seqs * a.num_kv_heads;
     const int64_t groups256 = rows * ((mq * a.group + 255) / 256);
     const int64_t groups128 = rows * ((mq * a.group + 127) / 128);
@@ -2194,15 +2275,15 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
             return prefill_pp_launch<128, 2>(a, s, blocks, mq);
         if (groups128 >= 256)
             return prefill_db_launch<128, 1, 8, 2>(a, s, blocks, mq);
-        return prefill_ws_launch<128, 8, 2, false>(a, s, blocks, mq);
+        return prefill_ss_launch<128, 2>(a, s, blocks, mq);
     case 256:
         if (groups128 >= 256)
             return prefill_db_launch<256, 1, 8, 2>(a, s, blocks, mq);
-        return prefill_ws_launch<256, 8, 2, false>(a, s, blocks, mq);
+        return prefill_ss_launch<256, 2>(a, s, blocks, mq);
     case 512:
         if (groups128 >= 512)
             return prefill_sb_launch<512, 1, 8, 2>(a, s, blocks, mq);
-        return prefill_ws_launch<512, 8, 2, true>(a, s, blocks, mq);
+        return prefill_ws_launch<512, 8, 2>(a, s, blocks, mq);
     default: return hipErrorInvalidValue;
     }
 }

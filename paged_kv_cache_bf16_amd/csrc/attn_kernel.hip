@@ -918,8 +918,9 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
 // max_tiles slots).  The fold factor of tile t depends only on the running
 // max before t -- the max of the earlier tile maxima, exact in any order,
 // whose reference is the state's reference -- so all factors come from one
-// prefix-max scan; wave 0 then runs the
-// dependent FMA chain in ascending tile order and writes the BF16 output.
+// prefix-max scan, stored per tile as one (gs, h) pair; then wave 0 runs
+// the dependent ACC chain (one dim per lane) and wave 1 the L chain, each in
+// ascending tile order, and wave 0 writes the BF16 output.
 constexpr int kFoldSlice = 64;
 constexpr int kFoldTiles = 192;
 constexpr int kFoldUnits = kFoldTiles * (kFoldSlice / 4) / NT;   // 16-byte loads per thread per round
@@ -964,8 +965,9 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
     using G = Geo<D>;
     constexpr int NSL = D / kFoldSlice;
     __shared__ float stage[kFoldTiles][kFoldSlice];
-    __shared__ float sm[kFoldTiles], sl[kFoldTiles], sg[kFoldTiles], sh[kFoldTiles];
-    __shared__ float wmax[NW];
+    __shared__ float sm[kFoldTiles], sl[kFoldTiles];
+    __shared__ float2 sgh[kFoldTiles];         // (gs, h) of each tile: one LDS read per tile in the chains
+    __shared__ float wmax[NW], sL;
 
     const int slice = blockIdx.x % NSL;
     const int col = blockIdx.x / NSL;
@@ -1015,22 +1017,30 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
         excl = lane == 0 ? pre : excl;
         if (th < nt) {
             const FoldF f = fold_factors(ref_of(excl), sm[th]);
-            sg[th] = f.gs;
-            sh[th] = f.h;
+            sgh[th] = make_float2(f.gs, f.h);
         }
         __syncthreads();
-        if (th < kFoldSlice) {
+        // wave 0 folds ACC (one dim per lane), wave 1 folds L, side by side;
+        // every thread carries M (the next round's scan starts from it)
+        if (w == 0) {
 #pragma unroll 8
-            for (int tt = 0; tt < nt; ++tt)
-                acc = fold1v(acc, stage[tt][th], sg[tt], sh[tt]);
+            for (int tt = 0; tt < nt; ++tt) {
+                const float2 gh = sgh[tt];
+                acc = fold1v(acc, stage[tt][th], gh.x, gh.y);
+            }
+        } else if (w == 1) {
+#pragma unroll 8
+            for (int tt = 0; tt < nt; ++tt) {
+                const float2 gh = sgh[tt];
+                L = fold1v(L, sl[tt], gh.x, gh.y);
+            }
         }
-        // every thread carries (M, L): the next round's scan starts from M,
-        // the running max after this round
-#pragma unroll 8
-        for (int tt = 0; tt < nt; ++tt)
-            L = fold1v(L, sl[tt], sg[tt], sh[tt]);
         M = total;
     }
+    if (th == 64)
+        sL = L;
+    __syncthreads();
+    L = sL;
     if (th < kFoldSlice) {
         const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
         a.out[ci.row * a.out_token_stride + (int64_t)ci.head * D + d0 + th] = finish1(acc, 1.0f / L);

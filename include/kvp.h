@@ -26,6 +26,15 @@
  *     never allocates device memory.
  *   - Work is queued on the caller's stream (a hipStream_t passed as void*;
  *     NULL is the default stream).  No entry point synchronises the host.
+ *   - Every launching entry point may be captured into a HIP graph: none
+ *     allocates, synchronises or issues a memset, and the launch shapes
+ *     depend only on host arguments (num_seqs, max_query_len, max_seq_len,
+ *     num_tokens).  A captured call replays with changed device metadata;
+ *     a row leaves a captured batch by getting seq_len 0 and no queries (its
+ *     table row sanitised by kv_prepare_block_tables), and its output rows
+ *     are then not written ("fix(rocm): stabilize direct paged CK attention
+ *     for bitwise R/R", Changes: inactive graph rows; Additional checks:
+ *     graph batches shrinking 4 -> 3 -> 2 -> 1).
  *   - BF16 values are passed as raw 16-bit patterns (uint16_t storage).
  *   - No C++ exception crosses this interface.
  */

@@ -740,7 +740,8 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     const int64_t hoff = (int64_t)kvh * BS * D;
 
 
-    // ---- issue every load of this workgroup up front
+    // ---- issue every load of this workgroup up front (non-temporal: each
+    // K/V byte is read once per call, so the lines need not stay cached)
     Cols<D> cols;
     const ColInfo ci = col_info(a, c, kvh, q0, q_len, seq_len);
     load_q<D>(cols, a, ci);
@@ -754,7 +755,7 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
         const uint16_t *pg = a.k_cache + bk * a.k_block_stride + hoff + tok * 8 + g * 128;
 #pragma unroll
         for (int ds = 0; ds < G::NDS; ++ds)
-            kf[kl][ds] = *reinterpret_cast<const bf16x8 *>(pg + ds * 512);
+            kf[kl][ds] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(pg + ds * 512));
     }
     u32x4 vraw[DPW][G::NKS];
 #pragma unroll
@@ -763,7 +764,7 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
         const uint16_t *pg = a.v_cache + bv * a.v_block_stride + hoff + 8 * (g & 1) + c * 16;
 #pragma unroll
         for (int dl = 0; dl < DPW; ++dl)
-            vraw[dl][st] = *reinterpret_cast<const u32x4 *>(pg + (16 * (w * DPW + dl)) * 16);
+            vraw[dl][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(pg + (16 * (w * DPW + dl)) * 16));
     }
     // keep every load above ahead of the first use of any of them
     __builtin_amdgcn_sched_barrier(0);

@@ -9,12 +9,16 @@ Headline (default --workload decode): B=4 sequences, one query each, KV
 length 7168, Hq 8 / Hkv 2 / Dh 128, 16-token pages permuted at random.  The
 pool holds 40 disjoint page sets (1.17 GB, well above the 256 MB Infinity
 Cache) and step i uses set i % 40, so every step reads K/V from HBM.
+The timed steps are replayed from HIP graphs that each hold 40 consecutive
+steps (the library's calls are capture-safe), so host launch work does not
+sit between steps; the eagerly issued rate is reported beside it.
 value = decode KV-read bytes per step / step time (GB/s).  The causal
 prefill B=1 Q=KV=4096 Hq 32 / Hkv 8 is measured in the same run and
 reported under "prefill" (TFLOP/s vs the BF16 MFMA peak).
 
-Roofline: the dominant kernel's average duration is timed live with HIP
-events around back-to-back launches on the launch stream; algorithmic bytes
+Roofline: the dominant kernels' average duration (one paged_attention call:
+partial + fold) is timed live with HIP events around graph replays of 40
+calls on the launch stream; algorithmic bytes
 (or FLOPs) per launch / that duration, against MI355X peaks (HBM 8 TB/s,
 dense BF16 MFMA 2.5 PFLOP/s).  cpu_baseline: the CPU oracle timed on this
 host on a bounded sample of the same workload.
@@ -122,47 +126,29 @@ class DecodeBench:
         self.kvp.paged_attention(self.pool, self.q[s], self.out, self.Hq, self.bt[s], self.sl, self.qsl, 1, self.L,
                                  self.scale, True, workspace=self.ws)
 
-    def step(self):
-        # reshape_and_cache of the 4 new tokens + decode attention, through kvp_decode_step
-        s = self.i % self.S
-        self.i += 1
+    def step_set(self, s):
+        # one step on page set s: reshape_and_cache of the 4 new tokens + decode
+        # attention, through kvp_decode_step (one partial launch + the fold)
         self.kvp.kvp_decode_step(self.pool, self.knew[s], self.vnew[s], self.slot_new[s], self.q[s], self.out,
                                  self.Hq, self.bt[s], self.sl, self.qsl, 1, self.L, self.scale, True,
                                  workspace=self.ws)
 
-    def capture_graphs(self):
-        """One HIP graph per page set holding that set's decode step (replayed in rotation)."""
-        import torch
-        self.graphs = []
-        for s in range(self.S):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                self.kvp.kvp_decode_step(self.pool, self.knew[s], self.vnew[s], self.slot_new[s], self.q[s],
-                                         self.out, self.Hq, self.bt[s], self.sl, self.qsl, 1, self.L, self.scale,
-                                         True, workspace=self.ws)
-            self.graphs.append(g)
-        torch.cuda.synchronize()
-
-    def capture_chain(self):
-        """One HIP graph holding the decode steps of all S page sets in order:
-        one replay runs S steps with no host work between them."""
-        import torch
-        self.chain = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.chain):
-            for s in range(self.S):
-                self.kvp.kvp_decode_step(self.pool, self.knew[s], self.vnew[s], self.slot_new[s], self.q[s],
-                                         self.out, self.Hq, self.bt[s], self.sl, self.qsl, 1, self.L, self.scale,
-                                         True, workspace=self.ws)
-        torch.cuda.synchronize()
-
-    def graph_step(self):
+    def step(self):
         s = self.i % self.S
         self.i += 1
-        self.graphs[s].replay()
+        self.step_set(s)
 
-    def attention_lse(self):
-        s = self.i % self.S
-        self.i += 1
+    def capture(self, fn, n):
+        """One HIP graph holding fn(s) for page sets s = 0 .. n-1 in order (no host work between them)."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(n):
+                fn(s)
+        torch.cuda.synchronize()
+        return g
+
+    def attention_lse(self, s):
         self.kvp.paged_attention_lse(self.pool, self.q[s], self.out, self.lse, self.Hq, self.bt[s], self.sl,
                                      self.qsl, 1, self.L, self.scale, True, workspace=self.ws)
 
@@ -346,44 +332,56 @@ def main():
     log("decode parity: max_abs=%.3g mean_abs=%.3g" % (mx, mean))
     assert mx <= 2e-2 and mean <= 2e-3, "decode output out of tolerance"
 
+    # eager issue first (kernels loaded, and the eager rate for reference)
     for _ in range(args.warmup):
         dec.step()
+    torch.cuda.synchronize()
+    eager_us = time_launches(dec.step, args.steps, stream)
+    log("decode, eager issue: %.2f us/step" % eager_us)
+
+    # timed steps: replayed from HIP graphs that hold the S page sets' steps in
+    # order, so no host launch work sits between steps (issued eagerly from
+    # Python, two kernel launches alone take ~10 us)
+    full, rem = divmod(args.steps, dec.S)
+    g_full = dec.capture(dec.step_set, dec.S)
+    g_rem = dec.capture(dec.step_set, rem) if rem else None
+    for _ in range(max(1, -(-args.warmup // dec.S))):
+        g_full.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for _ in range(args.steps):
-        dec.step()
+    for _ in range(full):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / args.steps
     log("decode: %.2f us/step (wall %.2f us/step)" % (ms_step * 1e3, wall / args.steps * 1e6))
+    del g_full, g_rem
 
-    # dominant kernel alone: 7 groups x 200 back-to-back launches, median
-    groups = [time_launches(dec.attention_only, 200, stream) for _ in range(7)]
+    # dominant kernels alone (one paged_attention call: partial + fold): a graph
+    # of S calls over the rotating page sets, 7 groups of 5 replays, median
+    g_attn = dec.capture(dec.attention, dec.S)
+    g_attn.replay()
+    groups = [time_launches(g_attn.replay, 5, stream) / dec.S for _ in range(7)]
     attn_us = float(np.median(groups))
     log("decode attention: %.2f us/call (groups %s)" % (attn_us, ["%.2f" % g for g in groups]))
-    # the same with the pool warm in the Infinity Cache (one page set)
+    del g_attn
+    g_lse = dec.capture(dec.attention_lse, dec.S)
+    g_lse.replay()
+    lse_us = float(np.median([time_launches(g_lse.replay, 5, stream) / dec.S for _ in range(5)]))
+    log("decode attention with lse: %.2f us/call" % lse_us)
+    del g_lse
+    # the same with the pool warm in the Infinity Cache (one page set), eager
     warm_us = time_launches(lambda: dec.attention(0), 400, stream)
+    eager_attn_us = float(np.median([time_launches(dec.attention_only, 200, stream) for _ in range(5)]))
 
     c0 = kvp.kvp_get_counters()
-    assert c0["split_kv_launches"] > 0
-
-    # the same decode step replayed from HIP graphs (one per page set)
-    dec.capture_graphs()
-    for _ in range(args.warmup):
-        dec.graph_step()
-    g_us = time_launches(dec.graph_step, args.steps, stream)
-    log("decode step from graphs: %.2f us/step" % g_us)
-    dec.capture_chain()
-    dec.chain.replay()
-    reps = max(1, args.steps // dec.S)
-    chain_us = time_launches(dec.chain.replay, reps, stream) / dec.S
-    log("decode step from a %d-step graph: %.2f us/step" % (dec.S, chain_us))
-    lse_us = float(np.median([time_launches(dec.attention_lse, 200, stream) for _ in range(5)]))
-    log("decode attention with lse: %.2f us/call" % lse_us)
+    assert c0["split_kv_launches"] > 0 and c0["fused_decode_steps"] > 0
 
     # merge of two results over disjoint key sets at the prefill shape (4096 tokens x 32 heads x 128)
     mg = MergeBench()
@@ -406,8 +404,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode B4 Q1 KV7168 Hq8 Hkv2 Dh128 page16 (random page permutation), "
                                "%d rotating page sets over a %.2f GB pool; step = kvp_decode_step: reshape_and_cache of "
-                               "the 4 new tokens + split-KV decode (cache write fused into the partial kernel)"
-                               % (dec.S, dec.S * dec.kv_bytes / 1e9),
+                               "the 4 new tokens + split-KV decode (cache write fused into the partial kernel); steps "
+                               "replayed from HIP graphs of %d consecutive steps" % (dec.S, dec.S * dec.kv_bytes / 1e9,
+                                                                                 dec.S),
                    "global_batch": dec.B, "seq_len": dec.L, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(dec.algo_bytes / (attn_us * 1e-6) / 1e9, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -417,12 +416,9 @@ def main():
                      "kernel": "split_partial_kernel<128> + split_fold_kernel<128> (one paged_attention call)",
                      "us_per_call": round(attn_us, 3),
                      "algo_bytes_per_call": dec.algo_bytes},
-        "decode_graph": {"us_per_step": round(g_us, 3), "GBps": round(dec.algo_bytes / (g_us * 1e-6) / 1e9, 2),
-                         "note": "the same step replayed from one captured HIP graph per page set"},
-        "decode_graph_chain": {"us_per_step": round(chain_us, 3),
-                               "GBps": round(dec.algo_bytes / (chain_us * 1e-6) / 1e9, 2),
-                               "note": "the %d page sets' steps captured in order in one graph; no host work "
-                                       "between steps" % dec.S},
+        "decode_eager": {"us_per_step": round(eager_us, 3), "GBps": round(dec.algo_bytes / (eager_us * 1e-6) / 1e9, 2),
+                         "attention_us_per_call": round(eager_attn_us, 3),
+                         "note": "the same steps issued one by one from Python (host launch cost included)"},
         "decode_lse": {"us_per_call": round(lse_us, 3), "note": "paged_attention_lse on the decode workload"},
         "merge": {"workload": "kvp_merge_attention of two [4096, 32, 128] BF16 results with FP32 lse",
                   "us_per_call": round(m_us, 3), "bytes_per_call": MergeBench.bytes,

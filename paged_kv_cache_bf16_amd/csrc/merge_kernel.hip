@@ -15,7 +15,8 @@
 // One pair takes head_dim / 8 consecutive lanes of one wave (16 bytes each),
 // so a wave reads and writes whole consecutive rows, and every lane of a
 // pair reads its lse values before the pair's lse is stored (in-place
-// merges, out == out_a and lse == lse_a, are safe).
+// merges, out == out_a and lse == lse_a, are safe).  Rows are read and
+// written with non-temporal accesses: each byte is touched once.
 #include "kvp_internal.h"
 
 namespace kvp {
@@ -46,8 +47,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m)
         return;
     const int64_t off = pair * m.head_dim + chunk * 8;
     const float la = m.lse_a[pair], lb = m.lse_b[pair];
-    const u32x4 ra = *reinterpret_cast<const u32x4 *>(m.out_a + off);
-    const u32x4 rb = *reinterpret_cast<const u32x4 *>(m.out_b + off);
+    const u32x4 ra = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(m.out_a + off));
+    const u32x4 rb = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(m.out_b + off));
 
     const float M = la > lb ? la : lb;
     u32x4 r = {0u, 0u, 0u, 0u};
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m)
         }
         lse = __builtin_fmaf(__builtin_amdgcn_logf(wt), 0.693147180559945309f, M);
     }
-    *reinterpret_cast<u32x4 *>(m.out + off) = r;
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x4 *>(m.out + off));
     if (m.lse && chunk == 0)
         m.lse[pair] = lse;
 }

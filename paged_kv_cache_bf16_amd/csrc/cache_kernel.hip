@@ -7,13 +7,16 @@
 //   K page [D/8][16 tokens][8]  -> one token's 8-dim group is a 16-byte unit,
 //   V page [D][16 tokens]       -> one token's value of dim d is 2 bytes at d*32.
 //
-// The work is HBM-bound (read + write of 2 * T * Hkv * D * 2 bytes).
-//   K: one lane per 16-byte unit; reads are contiguous across lanes and each
-//      store is a whole 16-byte unit.
-//   V: lanes walk consecutive tokens of one (head, 8-dim group), so the 2-byte
-//      stores of neighbouring lanes fall next to each other inside a page row
-//      whenever consecutive tokens occupy consecutive slots (the usual case);
-//      arbitrary slot mappings stay correct, only less coalesced.
+// The work is HBM-bound (read + write of 2 * T * Hkv * D * 2 bytes).  One
+// workgroup takes 16 consecutive tokens of one kv head: their K and V rows
+// are read whole (each token's head_dim values are contiguous) into LDS, then
+// written out in the page layouts:
+//   K: 16-byte units (dim group, token), token fastest across lanes, so a
+//      page's run of tokens is one contiguous stretch per dim group;
+//   V: 16-byte units of 8 tokens of one dim when those 8 tokens sit in 8
+//      consecutive slots starting at a multiple of 8 (a run inside one page,
+//      the usual case), otherwise one 2-byte store per token, so arbitrary
+//      slot mappings stay exact.
 // Block addresses are computed in 64-bit (pools beyond 2 GB).
 #include "kvp_internal.h"
 
@@ -22,67 +25,84 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void cache_k(const CacheArgs &a, int64_t blk_id)
-{
-    const int units_per_head = a.head_dim / 8;
-    const int64_t units = a.num_tokens * a.num_kv_heads * units_per_head;
-    const int64_t u = blk_id * blockDim.x + threadIdx.x;
-    if (u >= units)
-        return;
-    const int du = (int)(u % units_per_head);
-    const int64_t th = u / units_per_head;
-    const int h = (int)(th % a.num_kv_heads);
-    const int64_t i = th / a.num_kv_heads;
-    const int64_t s = a.slot_mapping[i];
-    if (s < 0 || s >= a.num_blocks * KVP_BLOCK_SIZE)
-        return;
-    const int64_t blk = s / KVP_BLOCK_SIZE;
-    const int t = (int)(s % KVP_BLOCK_SIZE);
-    const u32x4 val = *reinterpret_cast<const u32x4 *>(a.k + i * a.k_token_stride + (int64_t)h * a.head_dim + du * 8);
-    uint16_t *dst = a.k_cache + blk * a.k_block_stride + (int64_t)h * KVP_BLOCK_SIZE * a.head_dim
-                  + du * (KVP_BLOCK_SIZE * 8) + t * 8;
-    *reinterpret_cast<u32x4 *>(dst) = val;
-}
+constexpr int kChunk = 16;          // tokens per workgroup
+constexpr int kCacheThreads = 256;
 
-// Waves cover (head, dim-group) x token-chunks of 64; lane = token in chunk.
-__device__ __forceinline__ void cache_v(const CacheArgs &a, int64_t blk_id)
+template <int D>
+__global__ __launch_bounds__(kCacheThreads) void cache_kernel(CacheArgs a)
 {
-    const int units_per_head = a.head_dim / 8;
-    const int64_t chunks = (a.num_tokens + 63) / 64;
-    const int64_t w = (blk_id * blockDim.x + threadIdx.x) / 64;   // wave id
-    const int lane = threadIdx.x % 64;
-    const int64_t per_token_units = (int64_t)a.num_kv_heads * units_per_head;
-    if (w >= chunks * per_token_units)
-        return;
-    const int64_t hu = w % per_token_units;          // (head, dim group)
-    const int64_t i = (w / per_token_units) * 64 + lane;
-    if (i >= a.num_tokens)
-        return;
-    const int h = (int)(hu / units_per_head);
-    const int du = (int)(hu % units_per_head);
-    const int64_t s = a.slot_mapping[i];
-    if (s < 0 || s >= a.num_blocks * KVP_BLOCK_SIZE)
-        return;
-    const int64_t blk = s / KVP_BLOCK_SIZE;
-    const int t = (int)(s % KVP_BLOCK_SIZE);
-    const u32x4 val = *reinterpret_cast<const u32x4 *>(a.v + i * a.v_token_stride + (int64_t)h * a.head_dim + du * 8);
-    uint16_t *dst = a.v_cache + blk * a.v_block_stride + (int64_t)h * KVP_BLOCK_SIZE * a.head_dim
-                  + (int64_t)(du * 8) * KVP_BLOCK_SIZE + t;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        dst[(2 * j) * KVP_BLOCK_SIZE] = (uint16_t)(val[j] & 0xFFFFu);
-        dst[(2 * j + 1) * KVP_BLOCK_SIZE] = (uint16_t)(val[j] >> 16);
+    constexpr int UPT = D / 8;                          // 16-byte units per token row
+    constexpr int UNITS = kChunk * UPT;                 // per chunk, for K (and for V)
+    static_assert(UNITS % kCacheThreads == 0, "whole units per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t kl[kChunk][D];
+    __shared__ __attribute__((aligned(16))) uint16_t vl[kChunk][D];
+    __shared__ int64_t sl[kChunk];
+
+    const int64_t chunk = blockIdx.x / a.num_kv_heads;
+    const int h = (int)(blockIdx.x % a.num_kv_heads);
+    const int64_t i0 = chunk * kChunk;
+    const int nt = (int)min((int64_t)kChunk, a.num_tokens - i0);
+    const int th = threadIdx.x;
+    const int64_t nslots = a.num_blocks * KVP_BLOCK_SIZE;
+
+    if (th < kChunk) {
+        const int64_t s = th < nt ? a.slot_mapping[i0 + th] : -1;
+        sl[th] = (s >= 0 && s < nslots) ? s : -1;       // slots beyond the pool are skipped
     }
-}
+#pragma unroll
+    for (int r = 0; r < UNITS / kCacheThreads; ++r) {
+        const int u = th + r * kCacheThreads;
+        const int tok = u / UPT, du = u % UPT;
+        if (tok < nt) {
+            const int64_t i = i0 + tok;
+            *reinterpret_cast<u32x4 *>(&kl[tok][8 * du]) =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.k + i * a.k_token_stride + (int64_t)h * D + 8 * du));
+            *reinterpret_cast<u32x4 *>(&vl[tok][8 * du]) =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.v + i * a.v_token_stride + (int64_t)h * D + 8 * du));
+        }
+    }
+    __syncthreads();
 
-// One launch for both halves: workgroups [0, k_blocks) copy K, the rest V.
-__global__ __launch_bounds__(256) void cache_kernel(CacheArgs a, int64_t k_blocks)
-{
-    const int64_t bid = blockIdx.x;
-    if (bid < k_blocks)
-        cache_k(a, bid);
-    else
-        cache_v(a, bid - k_blocks);
+    const int64_t hoff = (int64_t)h * KVP_BLOCK_SIZE * D;
+    // K: unit (du, tok), token fastest
+#pragma unroll
+    for (int r = 0; r < UNITS / kCacheThreads; ++r) {
+        const int u = th + r * kCacheThreads;
+        const int tok = u % kChunk, du = u / kChunk;
+        const int64_t s = sl[tok];
+        if (tok < nt && s >= 0) {
+            uint16_t *dst = a.k_cache + (s / KVP_BLOCK_SIZE) * a.k_block_stride + hoff + du * (KVP_BLOCK_SIZE * 8)
+                          + (s % KVP_BLOCK_SIZE) * 8;
+            *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(&kl[tok][8 * du]);
+        }
+    }
+    // V: unit (dim d, half of the chunk's tokens)
+#pragma unroll
+    for (int r = 0; r < UNITS / kCacheThreads; ++r) {
+        const int u = th + r * kCacheThreads;
+        const int half = u % 2, d = u / 2;
+        const int t0 = 8 * half;
+        const int64_t s0 = sl[t0];
+        bool run = t0 + 8 <= nt && s0 >= 0 && (s0 % 8) == 0;
+#pragma unroll
+        for (int k = 1; k < 8; ++k)
+            run = run && sl[t0 + k] == s0 + k;
+        uint16_t *vbase = a.v_cache + hoff + (int64_t)d * KVP_BLOCK_SIZE;
+        if (run) {
+            u32x4 val;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                val[j] = (uint32_t)vl[t0 + 2 * j][d] | ((uint32_t)vl[t0 + 2 * j + 1][d] << 16);
+            *reinterpret_cast<u32x4 *>(vbase + (s0 / KVP_BLOCK_SIZE) * a.v_block_stride + s0 % KVP_BLOCK_SIZE) = val;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int64_t s = sl[t0 + k];
+                if (t0 + k < nt && s >= 0)
+                    vbase[(s / KVP_BLOCK_SIZE) * a.v_block_stride + s % KVP_BLOCK_SIZE] = vl[t0 + k][d];
+            }
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(u32x4 *p, int64_t n16)
@@ -96,15 +116,19 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(u32x4 *p, int64_t n16)
 
 hipError_t launch_reshape_and_cache(const CacheArgs &a, hipStream_t s, uint64_t *blocks)
 {
-    const int64_t units = a.num_tokens * a.num_kv_heads * (a.head_dim / 8);
-    const int64_t gk = (units + 255) / 256;
-    const int64_t waves = ((a.num_tokens + 63) / 64) * a.num_kv_heads * (a.head_dim / 8);
-    const int64_t gv = (waves + 3) / 4;
-    if (gk + gv > 0x7fffffff)
+    const int64_t grid = (a.num_tokens + kChunk - 1) / kChunk * a.num_kv_heads;
+    *blocks = 0;
+    if (grid <= 0)
+        return hipSuccess;
+    if (grid > 0x7fffffff)
         return hipErrorInvalidValue;
-    if (gk + gv > 0)
-        hipLaunchKernelGGL(cache_kernel, dim3((unsigned)(gk + gv)), dim3(256), 0, s, a, gk);
-    *blocks = (uint64_t)(gk + gv);
+    switch (a.head_dim) {
+    case 128: hipLaunchKernelGGL(cache_kernel<128>, dim3((unsigned)grid), dim3(kCacheThreads), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(cache_kernel<256>, dim3((unsigned)grid), dim3(kCacheThreads), 0, s, a); break;
+    case 512: hipLaunchKernelGGL(cache_kernel<512>, dim3((unsigned)grid), dim3(kCacheThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    *blocks = (uint64_t)grid;
     return hipGetLastError();
 }
 

@@ -251,8 +251,18 @@ class PrefillBench:
         self.kvp.paged_attention(self.pool, self.q, self.out, w.num_q_heads, self.bt, self.sl, self.qsl, self.L,
                                  self.L, w.scale, True)
 
-    def step(self):
+    def cache_write(self):
         self.kvp.reshape_and_cache(self.pool, self.k, self.v, self.slots)
+
+    @property
+    def cache_bytes(self):
+        # K and V rows read, the same bytes written into the pool, plus the slot ids
+        w = self.w
+        T = int(w.slot_mapping.shape[0])
+        return 2 * 2 * T * w.num_kv_heads * w.head_dim * 2 + 8 * T
+
+    def step(self):
+        self.cache_write()
         self.attention()
 
 
@@ -448,6 +458,13 @@ def main():
                              "kernel": "prefill_pp_kernel<128, 2>",
                              "hbm_traffic_bytes": recorded_traffic("prefill_pp_kernel<128,2>")}
         log("prefill: %.2f us/call, %.1f TFLOP/s" % (p_us, tf))
+        c_us = float(np.median([time_launches(pre.cache_write, 20, stream) for _ in range(5)]))
+        result["reshape_and_cache"] = {"workload": "4096 tokens x Hkv 8 x Dh 128 (K and V) into reversed pages; "
+                                                   "repeated on the same rows (warm Infinity Cache)",
+                                       "us_per_call": round(c_us, 3), "bytes_per_call": pre.cache_bytes,
+                                       "GBps": round(pre.cache_bytes / (c_us * 1e-6) / 1e9, 1),
+                                       "frac": round(pre.cache_bytes / (c_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log("reshape_and_cache: %.2f us/call" % c_us)
         del pre
 
     if not args.no_cpu_baseline:

@@ -1434,7 +1434,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
 
 // ---------------------------------------------------------------- wave-pair prefill
 
-// Two waves share each 16-column block: wave half h of the pair computes S
+// Two waves share CB 16-column blocks: wave half h of the pair computes S
 // for key blocks [h NKB/2, (h+1) NKB/2) of the tile and P.V for dim blocks
 // [h NDB/2, (h+1) NDB/2) of the output; the tile max, the per-lane partial
 // sums and P^T go through LDS.  Per column the arithmetic is the tile step of
@@ -1442,7 +1442,8 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
 // two halves of the same fixed tree (blocks of half 0, then of half 1, then
 // lanes xor 16 and xor 32); P^T and the fold are unchanged.  Used for
 // head_dim 512 grids too small for two 128-column workgroups per CU: half of
-// ACC per wave holds the state in registers without spills.
+// ACC per wave holds the state in registers without spills, and with CB = 2
+// every K and V fragment read from LDS feeds two MFMAs.
 
 template <int D>
 struct HalfState {
@@ -1451,15 +1452,16 @@ struct HalfState {
 };
 
 // Exchange area of one pair.
-template <int D>
+template <int D, int CB>
 struct PairX {
-    float mx[2][16];
-    float sum[2][64];
-    bf16x8 p[Geo<D>::NKS][64];
+    float mx[2][CB][16];
+    float sum[2][CB][64];
+    bf16x8 p[CB][Geo<D>::NKS][64];
 };
 
-template <int D>
-__device__ __forceinline__ void ws_qk(const char *kl, const Cols<D> &cols, f32x4 (&s)[Geo<D>::NKB / 2], int h)
+template <int D, int CB>
+__device__ __forceinline__ void ws_qk(const char *kl, const Cols<D> (&cols)[CB], f32x4 (&s)[CB][Geo<D>::NKB / 2],
+                                      int h)
 {
     using G = Geo<D>;
     constexpr int HK = G::NKB / 2;
@@ -1478,7 +1480,9 @@ __device__ __forceinline__ void ws_qk(const char *kl, const Cols<D> &cols, f32x4
 #pragma unroll
     for (int k = 0; k < HK; ++k) {
         kf[k] = *reinterpret_cast<const bf16x8 *>(base[k]);
-        s[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            s[cb][k] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int ds = 0; ds < G::NDS; ++ds) {
@@ -1489,114 +1493,131 @@ __device__ __forceinline__ void ws_qk(const char *kl, const Cols<D> &cols, f32x4
         }
 #pragma unroll
         for (int k = 0; k < HK; ++k)
-            s[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], cols.qf[ds], s[k], 0, 0, 0);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                s[cb][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], cols[cb].qf[ds], s[cb][k], 0, 0, 0);
 #pragma unroll
         for (int k = 0; k < HK; ++k)
             kf[k] = kn[k];
         if (ds + 1 < G::NDS)
             __builtin_amdgcn_sched_group_barrier(0x100, HK, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, HK, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, HK * CB, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // Stage 1: mask, this half's max of raw scores (exact), to the pair's area.
-template <int D, bool MASK>
-__device__ __forceinline__ void ws_max(f32x4 (&s)[Geo<D>::NKB / 2], int lim, int tile, int h, PairX<D> &x)
+template <int D, int CB, bool MASK>
+__device__ __forceinline__ void ws_max(f32x4 (&s)[CB][Geo<D>::NKB / 2], const Cols<D> (&cols)[CB], int tile, int h,
+                                       PairX<D, CB> &x)
 {
     using G = Geo<D>;
     constexpr int HK = G::NKB / 2;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, c = lane & 15;
-    float mk[HK];
 #pragma unroll
-    for (int k = 0; k < HK; ++k) {
-        if (MASK) {
-            const int kb = h * HK + k;
-            const int stp = kb >> 1, e = kb & 1;
+    for (int cb = 0; cb < CB; ++cb) {
+        float mk[HK];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = tile * G::T + 32 * stp + 8 * g + 4 * e + i;
-                s[k][i] = key < lim ? s[k][i] : -INFINITY;
+        for (int k = 0; k < HK; ++k) {
+            if (MASK) {
+                const int kb = h * HK + k;
+                const int stp = kb >> 1, e = kb & 1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = tile * G::T + 32 * stp + 8 * g + 4 * e + i;
+                    s[cb][k][i] = key < cols[cb].lim ? s[cb][k][i] : -INFINITY;
+                }
             }
+            mk[k] = fmax2(fmax2(s[cb][k][0], s[cb][k][1]), fmax2(s[cb][k][2], s[cb][k][3]));
         }
-        mk[k] = fmax2(fmax2(s[k][0], s[k][1]), fmax2(s[k][2], s[k][3]));
+#pragma unroll
+        for (int w = 1; w < HK; w *= 2)
+#pragma unroll
+            for (int k = 0; k < HK; k += 2 * w)
+                mk[k] = fmax2(mk[k], mk[k + w]);
+        const float m = max_xor32(max_xor16(mk[0]));
+        if (g == 0)
+            x.mx[h][cb][c] = m;
     }
-#pragma unroll
-    for (int w = 1; w < HK; w *= 2)
-#pragma unroll
-        for (int k = 0; k < HK; k += 2 * w)
-            mk[k] = fmax2(mk[k], mk[k + w]);
-    const float m = max_xor32(max_xor16(mk[0]));
-    if (g == 0)
-        x.mx[h][c] = m;
 }
 
 // Stage 2: the tile max, p, this half's level of the sum tree and its P^T
-// steps to the pair's area.  Returns m (scaled).
-template <int D>
-__device__ __forceinline__ float ws_exp(f32x4 (&s)[Geo<D>::NKB / 2], float scale_log2, int h, PairX<D> &x)
+// steps to the pair's area; m[cb] gets the scaled tile max.
+template <int D, int CB>
+__device__ __forceinline__ void ws_exp(f32x4 (&s)[CB][Geo<D>::NKB / 2], float scale_log2, int h, PairX<D, CB> &x,
+                                       float (&m)[CB])
 {
     using G = Geo<D>;
     constexpr int HK = G::NKB / 2;
     const int lane = threadIdx.x & 63;
     const int c = lane & 15;
-    const float m = __fmul_rn(fmax2(x.mx[0][c], x.mx[1][c]), scale_log2);
-    const float nmu = m == -INFINITY ? 0.f : -m;
-    float part[HK];
 #pragma unroll
-    for (int k = 0; k < HK; ++k) {
+    for (int cb = 0; cb < CB; ++cb) {
+        m[cb] = __fmul_rn(fmax2(x.mx[0][cb][c], x.mx[1][cb][c]), scale_log2);
+        const float nmu = m[cb] == -INFINITY ? 0.f : -m[cb];
+        float part[HK];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            s[k][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k][i], scale_log2, nmu));
-        part[k] = __fadd_rn(__fadd_rn(s[k][0], s[k][1]), __fadd_rn(s[k][2], s[k][3]));
-    }
+        for (int k = 0; k < HK; ++k) {
 #pragma unroll
-    for (int w = 1; w < HK; w *= 2)
-#pragma unroll
-        for (int k = 0; k < HK; k += 2 * w)
-            part[k] = __fadd_rn(part[k], part[k + w]);
-    x.sum[h][lane] = part[0];
-#pragma unroll
-    for (int sl = 0; sl < HK / 2; ++sl) {
-        bf16x8 pv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pv[i] = (__bf16)s[2 * sl][i];
-            pv[4 + i] = (__bf16)s[2 * sl + 1][i];
+            for (int i = 0; i < 4; ++i)
+                s[cb][k][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][k][i], scale_log2, nmu));
+            part[k] = __fadd_rn(__fadd_rn(s[cb][k][0], s[cb][k][1]), __fadd_rn(s[cb][k][2], s[cb][k][3]));
         }
-        x.p[h * (HK / 2) + sl][lane] = pv;
+#pragma unroll
+        for (int w = 1; w < HK; w *= 2)
+#pragma unroll
+            for (int k = 0; k < HK; k += 2 * w)
+                part[k] = __fadd_rn(part[k], part[k + w]);
+        x.sum[h][cb][lane] = part[0];
+#pragma unroll
+        for (int sl = 0; sl < HK / 2; ++sl) {
+            bf16x8 pv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pv[i] = (__bf16)s[cb][2 * sl][i];
+                pv[4 + i] = (__bf16)s[cb][2 * sl + 1][i];
+            }
+            x.p[cb][h * (HK / 2) + sl][lane] = pv;
+        }
     }
-    return m;
 }
 
 // Stage 3: l (the tree's last levels), the fold of (R, L), the rescale of
 // this half's ACC if some reference moved, then P.V for this half's dims
-// folded with fma(tile, h, ACC).
-template <int D, int DG>
-__device__ __forceinline__ void ws_fold_pv(const char *vl, float m, int h, const PairX<D> &x, HalfState<D> &st)
+// folded with fma(tile, h, ACC); each V fragment feeds all CB blocks.
+template <int D, int CB, int DG>
+__device__ __forceinline__ void ws_fold_pv(const char *vl, const float (&m)[CB], int h, const PairX<D, CB> &x,
+                                           HalfState<D> (&st)[CB])
 {
     using G = Geo<D>;
     constexpr int HD = G::NDB / 2;
     static_assert(HD % DG == 0, "whole groups");
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, c = lane & 15;
-    float l = __fadd_rn(x.sum[0][lane], x.sum[1][lane]);
-    l = sum_xor32(sum_xor16(l));
-    bf16x8 pf[G::NKS];
+    bf16x8 pf[CB][G::NKS];
+    FoldF f[CB];
+    bool any_up = false;
 #pragma unroll
-    for (int stp = 0; stp < G::NKS; ++stp)
-        pf[stp] = x.p[stp][lane];
-    const FoldF f = fold_factors(st.R, m);
-    const bool any_up = __ballot(f.up) != 0;
-    st.L = fold1v(st.L, l, f.gs, f.h);
-    st.R = f.Rn;
+    for (int cb = 0; cb < CB; ++cb) {
+        float l = __fadd_rn(x.sum[0][cb][lane], x.sum[1][cb][lane]);
+        l = sum_xor32(sum_xor16(l));
+#pragma unroll
+        for (int stp = 0; stp < G::NKS; ++stp)
+            pf[cb][stp] = x.p[cb][stp][lane];
+        f[cb] = fold_factors(st[cb].R, m[cb]);
+        any_up |= __ballot(f[cb].up) != 0;
+        st[cb].L = fold1v(st[cb].L, l, f[cb].gs, f[cb].h);
+        st[cb].R = f[cb].Rn;
+    }
     if (any_up) {
 #pragma unroll
-        for (int db = 0; db < HD; ++db)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                st.acc[db][i] = __fmul_rn(st.acc[db][i], f.gs);
+            for (int db = 0; db < HD; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st[cb].acc[db][i] = __fmul_rn(st[cb].acc[db][i], f[cb].gs);
     }
     auto vaddr = [&](int db, int stp) -> const char * {
         const int d = 16 * db + c;
@@ -1604,11 +1625,13 @@ __device__ __forceinline__ void ws_fold_pv(const char *vl, float m, int h, const
     };
 #pragma unroll
     for (int d0 = 0; d0 < HD; d0 += DG) {
-        f32x4 o[DG];
+        f32x4 o[CB][DG];
         bf16x8 vf[DG], vn[DG];
 #pragma unroll
         for (int d = 0; d < DG; ++d) {
-            o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                o[cb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
             vf[d] = *reinterpret_cast<const bf16x8 *>(vaddr(h * HD + d0 + d, 0));
         }
 #pragma unroll
@@ -1620,20 +1643,24 @@ __device__ __forceinline__ void ws_fold_pv(const char *vl, float m, int h, const
             }
 #pragma unroll
             for (int d = 0; d < DG; ++d)
-                o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], pf[stp], o[d], 0, 0, 0);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    o[cb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], pf[cb][stp], o[cb][d], 0, 0, 0);
 #pragma unroll
             for (int d = 0; d < DG; ++d)
                 vf[d] = vn[d];
             if (stp + 1 < G::NKS)
                 __builtin_amdgcn_sched_group_barrier(0x100, DG, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, DG, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, DG * CB, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int d = 0; d < DG; ++d)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                st.acc[d0 + d][i] = __builtin_fmaf(o[d][i], f.h, st.acc[d0 + d][i]);
+            for (int d = 0; d < DG; ++d)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st[cb].acc[d0 + d][i] = __builtin_fmaf(o[cb][d][i], f[cb].h, st[cb].acc[d0 + d][i]);
     }
 }
 
@@ -1660,10 +1687,9 @@ struct WsSetup {
     bool run;
 };
 
-template <int D, int NWV>
+template <int D, int NCOL>
 __device__ __forceinline__ WsSetup ws_setup(const AttnArgs &a)
 {
-    constexpr int NCOL = NWV / 2 * 16;
     WsSetup w{};
     w.run = false;
     const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
@@ -1693,12 +1719,12 @@ __device__ __forceinline__ WsSetup ws_setup(const AttnArgs &a)
 // Single-buffered wave-pair kernel (head_dim 512, whose K+V tile takes 128
 // KB of LDS): the staging order of prefill_sb_kernel; the pair exchanges
 // share its barriers (the maxima with "K(t) read", P^T and the sums with
-// "V(t) landed").
-template <int D, int NWV, int WPE>
+// "V(t) landed").  NWV / 2 pairs of CB column blocks each.
+template <int D, int NWV, int WPE, int CB>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void prefill_ws_sb_kernel(AttnArgs a)
 {
     using G = Geo<D>;
-    constexpr int NCOL = NWV / 2 * 16;
+    constexpr int NCOL = NWV / 2 * CB * 16;
     constexpr int HALF = G::NKB * G::PAGE;
     constexpr int CPP = G::PAGE / 1024;
     constexpr int CPW = G::NKB * CPP / NWV;
@@ -1707,30 +1733,36 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     extern __shared__ __attribute__((aligned(16))) char lds[];
     char *const kbuf = lds;
     char *const vbuf = lds + HALF;
-    int32_t *const ids = reinterpret_cast<int32_t *>(lds + 2 * HALF);                 // [2][NKB]
-    PairX<D> *const xs = reinterpret_cast<PairX<D> *>(lds + 2 * HALF + 2 * G::NKB * 4);   // [NWV / 2]
+    int32_t *const ids = reinterpret_cast<int32_t *>(lds + 2 * HALF);                     // [2][NKB]
+    PairX<D, CB> *const xs = reinterpret_cast<PairX<D, CB> *>(lds + 2 * HALF + 2 * G::NKB * 4);   // [NWV / 2]
 
-    const WsSetup w = ws_setup<D, NWV>(a);
+    const WsSetup w = ws_setup<D, NCOL>(a);
     if (!w.run)
         return;
     const int c = threadIdx.x & 15;
     const int32_t *bt_row = a.block_tables + (int64_t)w.b * a.bt_stride;
-    Cols<D> cols;
-    HalfState<D> st;
-    const int col = w.cg * NCOL + w.pair * 16 + c;
-    const ColInfo ci = col_info(a, col, w.kvh, w.q0, w.q_len, w.seq_len);
-    load_q<D>(cols, a, ci);
-    st.R = -INFINITY;
-    st.L = 0.f;
+    Cols<D> cols[CB];
+    HalfState<D> st[CB];
+    ColInfo ci[CB];
+    bool active = false;
+    int min_lim = 0x7fffffff;
 #pragma unroll
-    for (int db = 0; db < G::NDB / 2; ++db)
-        st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool active = w.cg * NCOL + w.pair * 16 < w.ncols;
-    int min_lim = cols.lim;
+    for (int cb = 0; cb < CB; ++cb) {
+        const int col = w.cg * NCOL + (w.pair * CB + cb) * 16 + c;
+        ci[cb] = col_info(a, col, w.kvh, w.q0, w.q_len, w.seq_len);
+        load_q<D>(cols[cb], a, ci[cb]);
+        st[cb].R = -INFINITY;
+        st[cb].L = 0.f;
+#pragma unroll
+        for (int db = 0; db < G::NDB / 2; ++db)
+            st[cb].acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        active |= w.cg * NCOL + (w.pair * CB + cb) * 16 < w.ncols;
+        min_lim = min(min_lim, cols[cb].lim);
+    }
 #pragma unroll
     for (int off = 1; off < 64; off *= 2)
         min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
-    PairX<D> &x = xs[w.pair];
+    PairX<D, CB> &x = xs[w.pair];
 
     auto lds_addr = [](const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p; };
     auto issue = [&](bool is_k, int tile) {
@@ -1765,20 +1797,20 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     __syncthreads();
 
     for (int t = 0; t <= w.last; ++t) {
-        f32x4 s[G::NKB / 2];
-        float m = 0.f;
+        f32x4 s[CB][G::NKB / 2];
+        float m[CB];
         if (active) {
-            ws_qk<D>(kbuf, cols, s, w.half);
+            ws_qk<D, CB>(kbuf, cols, s, w.half);
             if ((t + 1) * G::T > min_lim)
-                ws_max<D, true>(s, cols.lim, t, w.half, x);
+                ws_max<D, CB, true>(s, cols, t, w.half, x);
             else
-                ws_max<D, false>(s, cols.lim, t, w.half, x);
+                ws_max<D, CB, false>(s, cols, t, w.half, x);
         }
         __syncthreads();                                   // K(t) read by every wave; maxima visible
         if (t < w.last)
             issue(true, t + 1);
         if (active)
-            m = ws_exp<D>(s, a.scale_log2, w.half, x);
+            ws_exp<D, CB>(s, a.scale_log2, w.half, x, m);
         // V(t) (issued before K(t+1)) has landed
         if (t < w.last)
             wait_vm<CPW>();
@@ -1790,7 +1822,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             __syncthreads();
         }
         if (active)
-            ws_fold_pv<D, 4>(vbuf, m, w.half, x, st);
+            ws_fold_pv<D, CB, 4>(vbuf, m, w.half, x, st);
         __syncthreads();                                   // V(t) read by every wave
         if (t < w.last) {
             if (t + 2 <= w.last)
@@ -1801,8 +1833,10 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             __syncthreads();
         }
     }
-    if (ci.lim > 0)
-        ws_store<D>(a, ci, st, w.half);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        if (ci[cb].lim > 0)
+            ws_store<D>(a, ci[cb], st[cb], w.half);
 }
 
 // ---------------------------------------------------------------- producer / consumer prefill
@@ -2205,11 +2239,11 @@ static hipError_t prefill_db_launch(AttnArgs a, hipStream_t s, uint64_t *blocks,
     return hipGetLastError();
 }
 
-template <int D, int NWV, int WPE>
+template <int D, int NWV, int WPE, int CB>
 static hipError_t prefill_ws_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
 {
-    constexpr int NCOL = NWV / 2 * 16;
-    constexpr int LDS_BYTES = Geo<D>::LDS + 2 * Geo<D>::NKB * 4 + NWV / 2 * (int)sizeof(PairX<D>);
+    constexpr int NCOL = NWV / 2 * CB * 16;
+    constexpr int LDS_BYTES = Geo<D>::LDS + 2 * Geo<D>::NKB * 4 + NWV / 2 * (int)sizeof(PairX<D, CB>);
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
     const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;
@@ -2218,10 +2252,10 @@ static hipError_t prefill_ws_launch(AttnArgs a, hipStream_t s, uint64_t *blocks,
         return hipSuccess;
     if (grid > 0x7fffffff)
         return hipErrorInvalidValue;
-    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_ws_sb_kernel<D, NWV, WPE>,
+    static const hipError_t attr = hipFuncSetAttribute((const void *)prefill_ws_sb_kernel<D, NWV, WPE, CB>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     (void)attr;
-    hipLaunchKernelGGL((prefill_ws_sb_kernel<D, NWV, WPE>), dim3((unsigned)grid), dim3(NWV * 64), LDS_BYTES, s, a);
+    hipLaunchKernelGGL((prefill_ws_sb_kernel<D, NWV, WPE, CB>), dim3((unsigned)grid), dim3(NWV * 64), LDS_BYTES, s, a);
     *blocks = (uint64_t)grid;
     return hipGetLastError();
 }
@@ -2294,7 +2328,7 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
     case 512:
         if (groups128 >= 512)
             return prefill_sb_launch<512, 1, 8, 2>(a, s, blocks, mq);
-        return prefill_ws_launch<512, 8, 2>(a, s, blocks, mq);
+        return prefill_ws_launch<512, 8, 2, 1>(a, s, blocks, mq);
     default: return hipErrorInvalidValue;
     }
 }

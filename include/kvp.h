@@ -120,6 +120,17 @@ int reshape_and_cache(const kvp_pool *pool, const void *k, const void *v, int64_
                       const int64_t *slot_mapping, void *stream);
 
 /*
+ * kvp_check_slot_mapping -- host-side check of a slot mapping (a debug aid
+ * for the preconditions reshape_and_cache does not check on the device):
+ * every slot is < num_blocks * 16 and no two tokens share a slot; negative
+ * slots are allowed (skipped by the scatter).
+ *   slots  host, [num_tokens] int64.
+ * Errors: INVALID_ARGUMENT, naming the first offending token in
+ * kvp_last_error().
+ */
+int kvp_check_slot_mapping(const kvp_pool *pool, const int64_t *slots, int64_t num_tokens);
+
+/*
  * kv_prepare_block_tables -- page-table metadata prep, host only
  * ("fix(rocm): stabilize direct paged CK attention for bitwise R/R",
  * Changes: pad page tables to complete KV tiles and sanitise unused

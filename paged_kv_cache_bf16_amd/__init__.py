@@ -65,6 +65,7 @@ def load_library(path: str = LIB_PATH):
         "reshape_and_cache": ([P, P, P, I64, I64, I64, P, P], I),
         "kv_prepare_block_tables": ([P, P, ctypes.c_int32, ctypes.c_int32, P, P], I),
         "kvp_padded_width": ([ctypes.c_int32], ctypes.c_int32),
+        "kvp_check_slot_mapping": ([P, P, I64], I),
         "kvp_workspace_bytes": ([P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(SZ)], I),
         "kvp_workspace_init": ([P, SZ, P], I),
         "paged_attention": ([P, P, I64, P, I64, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P,
@@ -182,6 +183,12 @@ def reshape_and_cache(pool: KVPool, k, v, slot_mapping, stream=None) -> None:
 
 
 # ------------------------------------------------------------------ metadata
+
+
+def kvp_check_slot_mapping(pool: KVPool, slot_mapping) -> None:
+    """Host-side check: slots inside the pool and no slot used twice (raises KvpError)."""
+    s = np.ascontiguousarray(np.asarray(slot_mapping), dtype=np.int64)
+    _check(load_library().kvp_check_slot_mapping(pool.handle, s.ctypes.data_as(ctypes.c_void_p), int(s.shape[0])))
 
 
 def kvp_padded_width(width: int) -> int:

@@ -13,6 +13,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <unordered_map>
 
 #include "kvp_internal.h"
 
@@ -319,6 +320,28 @@ int32_t kvp_padded_width(int32_t width)
     if (width <= 0)
         return 8;
     return (int32_t)(cdiv(width, 8) * 8);
+}
+
+int kvp_check_slot_mapping(const kvp_pool *pool, const int64_t *slots, int64_t num_tokens)
+{
+    if (!pool || num_tokens < 0 || (num_tokens > 0 && !slots))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_check_slot_mapping: null pool or slots, or negative count");
+    const int64_t nslots = pool->d.num_blocks * KVP_BLOCK_SIZE;
+    std::unordered_map<int64_t, int64_t> first;
+    first.reserve((size_t)num_tokens);
+    for (int64_t i = 0; i < num_tokens; ++i) {
+        const int64_t s = slots[i];
+        if (s < 0)
+            continue;
+        if (s >= nslots)
+            return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_check_slot_mapping: token %lld has slot %lld beyond the pool (%lld)",
+                        (long long)i, (long long)s, (long long)nslots);
+        const auto r = first.emplace(s, i);
+        if (!r.second)
+            return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_check_slot_mapping: tokens %lld and %lld share slot %lld",
+                        (long long)r.first->second, (long long)i, (long long)s);
+    }
+    return ok();
 }
 
 int kv_prepare_block_tables(const kvp_pool *pool, const int32_t *block_tables, int32_t num_seqs,

@@ -233,3 +233,37 @@ def test_merge_empty_is_ok_without_launch(lib):
     kvp.kvp_reset_counters()
     assert lib.kvp_merge_attention(None, None, None, None, None, None, 0, 8, 128, None) == 0
     assert kvp.kvp_get_counters()["merge_launches"] == 0
+
+
+def test_check_slot_mapping_agrees_with_the_oracle(lib):
+    """The host-side slot check accepts exactly the mappings the oracle's
+    scatter accepts (negative slots skipped; duplicates and slots beyond the
+    pool rejected), on random mappings of a 6-block pool."""
+    rc, h = create(lib, num_blocks=6)
+    pool = kvp.KVPool(h, make_desc(num_blocks=6), None)
+    rng = np.random.default_rng(12)
+    seen = {True: 0, False: 0}
+    for trial in range(300):
+        n = int(rng.integers(1, 12))
+        slots = rng.integers(-3, 6 * 16 + 4, size=n).astype(np.int64)
+        if trial % 3 == 0:
+            slots = rng.permutation(6 * 16)[:n].astype(np.int64)        # always valid
+        opool = oracle.Pool(6, 2, 128)
+        kv = np.zeros((n, 2, 128), np.uint16)
+        try:
+            oracle.reshape_and_cache(opool, kv, kv, slots)
+            ok_oracle = True
+        except oracle.OracleError:
+            ok_oracle = False
+        try:
+            kvp.kvp_check_slot_mapping(pool, slots)
+            ok_lib = True
+        except kvp.KvpError as e:
+            ok_lib = False
+            assert e.code == kvp.KVP_ERR_INVALID_ARGUMENT
+            assert "share slot" in str(e) or "beyond the pool" in str(e)
+        assert ok_lib == ok_oracle, slots
+        seen[ok_lib] += 1
+    assert seen[True] > 50 and seen[False] > 50
+    kvp.kvp_check_slot_mapping(pool, np.array([], np.int64))
+    del pool                                  # the wrapper destroys the descriptor

@@ -699,9 +699,14 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     constexpr int KPW = G::NKB / NW;   // key blocks per wave
     constexpr int DPW = G::NDB / NW;   // dim blocks per wave
     static_assert(KPW == 1 || KPW == 2, "tile shape");
+    // head_dim 512: the Q fragments go through LDS (each wave loads a quarter
+    // of the dim steps), so the tile's K and V fit in registers with room for
+    // three workgroups per CU
+    constexpr bool QL = D == 512;
     __shared__ float smax[NW][16];
     __shared__ float ssum[NW][64];
     __shared__ uint32_t spf[NW][2 * KPW][64];
+    __shared__ bf16x8 sq[QL ? G::NDS : 1][64];
 
     const int tile = blockIdx.x;
     const int kvh = blockIdx.y;
@@ -744,7 +749,17 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     // K/V byte is read once per call, so the lines need not stay cached)
     Cols<D> cols;
     const ColInfo ci = col_info(a, c, kvh, q0, q_len, seq_len);
-    load_q<D>(cols, a, ci);
+    constexpr int QPW = G::NDS / NW;               // dim steps of Q each wave stages (QL)
+    bf16x8 qpart[QL ? QPW : 1];
+    if (QL) {
+        const uint16_t *src = a.q + (ci.lim > 0 ? ci.row : ci.row0) * a.q_token_stride + (int64_t)ci.head * D + 8 * g;
+#pragma unroll
+        for (int k = 0; k < QPW; ++k)
+            qpart[k] = *reinterpret_cast<const bf16x8 *>(src + 32 * (w * QPW + k));
+        cols.lim = ci.lim;
+    } else {
+        load_q<D>(cols, a, ci);
+    }
     bf16x8 kf[KPW][G::NDS];
 #pragma unroll
     for (int kl = 0; kl < KPW; ++kl) {
@@ -768,6 +783,12 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     }
     // keep every load above ahead of the first use of any of them
     __builtin_amdgcn_sched_barrier(0);
+    if (QL) {
+#pragma unroll
+        for (int k = 0; k < QPW; ++k)
+            sq[w * QPW + k][lane] = qpart[k];
+        __syncthreads();
+    }
 
     // ---- new tokens of this launch whose slots fall in this tile (FUSE):
     // their keys come from the new rows, not from the pool (reloaded only in
@@ -844,7 +865,8 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ds = 0; ds < G::NDS; ++ds)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kl][ds], cols.qf[ds], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kl][ds], QL ? sq[ds][lane] : cols.qf[QL ? 0 : ds], acc,
+                                                          0, 0, 0);
         const int kb = w * KPW + kl;
         const int st = kb >> 1, e = kb & 1;
 #pragma unroll

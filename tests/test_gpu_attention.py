@@ -445,3 +445,33 @@ def test_prefill_kernel_per_grid_size(lens, Hq, Hkv, D, ncol):
     d = w.decode_view()
     g.set_queries(d.q, d.query_lens)
     bitwise(g.run(), full[w.query_start_loc[1:] - 1], "decode vs prefill last rows (%s, D=%d)" % (lens, D))
+
+
+def _random_shape(rng):
+    D = int(rng.choice([128, 256, 512]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    B = int(rng.integers(1, 5))
+    max_len = 700 if D == 512 else 1500
+    seq = [int(x) for x in rng.integers(1, max_len, size=B)]
+    ql = []
+    for L in seq:
+        kind = int(rng.integers(0, 4))
+        ql.append({0: 1, 1: L, 2: min(L, max(1, 16 // G)), 3: int(rng.integers(1, L + 1))}[kind])
+    return seq, ql, Hkv * G, Hkv, D, bool(rng.integers(0, 4) > 0)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shape_sweep(seed):
+    """Seeded random shapes (head dims, group sizes 1..16, ragged lengths, q_len * G around
+    the split-KV threshold, causal and not): sampled rows against the oracle, with and
+    without a workspace (split-KV for short rows, or every row through a prefill kernel),
+    which must give the same bits."""
+    rng = np.random.default_rng(1000 + seed)
+    seq, ql, Hq, Hkv, D, causal = _random_shape(rng)
+    w = wl.random_case(2000 + seed, seq, ql, Hq, Hkv, D, causal=causal)
+    print("random shape", seq, ql, Hq, Hkv, D, causal, flush=True)
+    rows = sample_rows(w, 24, seed)
+    g, out, _ = _run_and_compare(w, rows=rows, what="random %d" % seed)
+    if w.batch > 1 and int(w.max_query_len) * (Hq // Hkv) > 16:
+        bitwise(g.run(use_workspace=False), out, "random %d: with vs without workspace" % seed)

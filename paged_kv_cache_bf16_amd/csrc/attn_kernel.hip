@@ -111,6 +111,32 @@ __device__ __forceinline__ float max_xor32(float v)
     return fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Max of N values in three-input steps (v_maximum3_f32): exact in any order,
+// so the reduction shape is free; this one needs about N / 2 instructions.
+template <int N>
+__device__ __forceinline__ float max_reduce(const float (&v)[N])
+{
+    if constexpr (N == 1) {
+        return v[0];
+    } else if constexpr (N == 2) {
+        return fmax2(v[0], v[1]);
+    } else {
+        constexpr int M = (N + 2) / 3;
+        float r[M];
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            const int a = 3 * i;
+            if (a + 2 < N)
+                r[i] = fmax2(fmax2(v[a], v[a + 1]), v[a + 2]);
+            else if (a + 1 < N)
+                r[i] = fmax2(v[a], v[a + 1]);
+            else
+                r[i] = v[a];
+        }
+        return max_reduce<M>(r);
+    }
+}
+
 // ---------------------------------------------------------------- staging
 
 // Block ids of the NKB pages of tile `tile` (wave-uniform), as one vector
@@ -488,7 +514,7 @@ __device__ __forceinline__ bool prefill_softmax_stats(f32x4 (&s)[CB][Geo<D>::NKB
     float mx[CB], lsum[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        float mk[G::NKB];
+        float vals[4 * G::NKB];
 #pragma unroll
         for (int kb = 0; kb < G::NKB; ++kb) {
             if (MASK) {
@@ -499,14 +525,11 @@ __device__ __forceinline__ bool prefill_softmax_stats(f32x4 (&s)[CB][Geo<D>::NKB
                     s[cb][kb][i] = key < cols[cb].lim ? s[cb][kb][i] : -INFINITY;
                 }
             }
-            mk[kb] = fmax2(fmax2(s[cb][kb][0], s[cb][kb][1]), fmax2(s[cb][kb][2], s[cb][kb][3]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vals[4 * kb + i] = s[cb][kb][i];
         }
-#pragma unroll
-        for (int w = 1; w < G::NKB; w *= 2)
-#pragma unroll
-            for (int kb = 0; kb < G::NKB; kb += 2 * w)
-                mk[kb] = fmax2(mk[kb], mk[kb + w]);
-        mx[cb] = mk[0];
+        mx[cb] = max_reduce<4 * G::NKB>(vals);
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
@@ -1539,7 +1562,7 @@ __device__ __forceinline__ void ws_max(f32x4 (&s)[CB][Geo<D>::NKB / 2], const Co
     const int g = lane >> 4, c = lane & 15;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        float mk[HK];
+        float vals[4 * HK];
 #pragma unroll
         for (int k = 0; k < HK; ++k) {
             if (MASK) {
@@ -1551,14 +1574,11 @@ __device__ __forceinline__ void ws_max(f32x4 (&s)[CB][Geo<D>::NKB / 2], const Co
                     s[cb][k][i] = key < cols[cb].lim ? s[cb][k][i] : -INFINITY;
                 }
             }
-            mk[k] = fmax2(fmax2(s[cb][k][0], s[cb][k][1]), fmax2(s[cb][k][2], s[cb][k][3]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vals[4 * k + i] = s[cb][k][i];
         }
-#pragma unroll
-        for (int w = 1; w < HK; w *= 2)
-#pragma unroll
-            for (int k = 0; k < HK; k += 2 * w)
-                mk[k] = fmax2(mk[k], mk[k + w]);
-        const float m = max_xor32(max_xor16(mk[0]));
+        const float m = max_xor32(max_xor16(max_reduce<4 * HK>(vals)));
         if (g == 0)
             x.mx[h][cb][c] = m;
     }

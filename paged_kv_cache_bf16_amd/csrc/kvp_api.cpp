@@ -19,25 +19,23 @@
 
 namespace {
 
-thread_local std::string g_err;
+thread_local char g_err[512];      // fixed storage: setting it cannot throw
 
 std::atomic<uint64_t> g_cache_launches{0}, g_split_launches{0}, g_prefill_launches{0},
     g_init_launches{0}, g_last_grid{0}, g_fused_steps{0}, g_merge_launches{0};
 
 int fail(int code, const char *fmt, ...)
 {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
     va_end(ap);
-    g_err = buf;
     return code;
 }
 
 int ok()
 {
-    g_err.clear();
+    g_err[0] = '\0';
     return KVP_OK;
 }
 
@@ -327,19 +325,24 @@ int kvp_check_slot_mapping(const kvp_pool *pool, const int64_t *slots, int64_t n
     if (!pool || num_tokens < 0 || (num_tokens > 0 && !slots))
         return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_check_slot_mapping: null pool or slots, or negative count");
     const int64_t nslots = pool->d.num_blocks * KVP_BLOCK_SIZE;
-    std::unordered_map<int64_t, int64_t> first;
-    first.reserve((size_t)num_tokens);
-    for (int64_t i = 0; i < num_tokens; ++i) {
-        const int64_t s = slots[i];
-        if (s < 0)
-            continue;
-        if (s >= nslots)
-            return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_check_slot_mapping: token %lld has slot %lld beyond the pool (%lld)",
-                        (long long)i, (long long)s, (long long)nslots);
-        const auto r = first.emplace(s, i);
-        if (!r.second)
-            return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_check_slot_mapping: tokens %lld and %lld share slot %lld",
-                        (long long)r.first->second, (long long)i, (long long)s);
+    try {
+        std::unordered_map<int64_t, int64_t> first;
+        first.reserve((size_t)num_tokens);
+        for (int64_t i = 0; i < num_tokens; ++i) {
+            const int64_t s = slots[i];
+            if (s < 0)
+                continue;
+            if (s >= nslots)
+                return fail(KVP_ERR_INVALID_ARGUMENT,
+                            "kvp_check_slot_mapping: token %lld has slot %lld beyond the pool (%lld)", (long long)i,
+                            (long long)s, (long long)nslots);
+            const auto r = first.emplace(s, i);
+            if (!r.second)
+                return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_check_slot_mapping: tokens %lld and %lld share slot %lld",
+                            (long long)r.first->second, (long long)i, (long long)s);
+        }
+    } catch (...) {     // allocation failure: no exception crosses the C ABI
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_check_slot_mapping: out of host memory");
     }
     return ok();
 }
@@ -561,7 +564,7 @@ int kvp_reset_counters(void)
     return ok();
 }
 
-const char *kvp_last_error(void) { return g_err.c_str(); }
+const char *kvp_last_error(void) { return g_err; }
 
 const char *kvp_version(void) { return "kvp 0.1 gfx950"; }
 

@@ -12,7 +12,6 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
-#include <string>
 #include <unordered_map>
 
 #include "kvp_internal.h"

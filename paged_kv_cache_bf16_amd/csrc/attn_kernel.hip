@@ -971,37 +971,55 @@ constexpr int kFoldSlice = 64;
 constexpr int kFoldTiles = 192;
 constexpr int kFoldUnits = kFoldTiles * (kFoldSlice / 4) / NT;   // 16-byte loads per thread per round
 
+// One round of the fold's inputs: the (acc, m, l) partials of tiles
+// t0 .. t0+nt-1 for one column and one 64-dim slice.  fold_load issues the
+// loads (rounds of whole workgroups past the last tile issue none);
+// fold_store waits for them and writes them to LDS.
+struct FoldRound {
+    f32x4 v[kFoldUnits];
+    float m, l;
+};
+
 template <int D>
-__device__ __forceinline__ void fold_stage(const AttnArgs &a, int64_t slot0, int col, int d0, int t0, int nt,
-                                           float (*stage)[kFoldSlice], float *sm, float *sl)
+__device__ __forceinline__ void fold_load(const AttnArgs &a, int64_t slot0, int col, int d0, int t0, int nt,
+                                          FoldRound &fr)
 {
     const int th = threadIdx.x;
-    f32x4 v[kFoldUnits];
 #pragma unroll
     for (int r = 0; r < kFoldUnits; ++r) {
+        if (r * NT >= nt * (kFoldSlice / 4))
+            break;
         const int u = th + r * NT;
         const int tt = min(u / (kFoldSlice / 4), nt - 1);
         const int q = u % (kFoldSlice / 4);
         const int64_t si = (slot0 + t0 + tt) * kSplitCols + col;
-        v[r] = *reinterpret_cast<const f32x4 *>(a.ws_acc + si * D + d0 + 4 * q);
+        fr.v[r] = *reinterpret_cast<const f32x4 *>(a.ws_acc + si * D + d0 + 4 * q);
     }
-    float m = 0.f, l = 0.f;
+    fr.m = 0.f;
+    fr.l = 0.f;
     if (th < kFoldTiles) {
         const int64_t si = (slot0 + t0 + min(th, nt - 1)) * kSplitCols + col;
-        m = a.ws_m[si];
-        l = a.ws_l[si];
+        fr.m = a.ws_m[si];
+        fr.l = a.ws_l[si];
     }
-    __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void fold_store(const FoldRound &fr, int nt, float (*stage)[kFoldSlice], float *sm,
+                                           float *sl)
+{
+    const int th = threadIdx.x;
 #pragma unroll
     for (int r = 0; r < kFoldUnits; ++r) {
+        if (r * NT >= nt * (kFoldSlice / 4))
+            break;
         const int u = th + r * NT;
         const int tt = u / (kFoldSlice / 4);
         if (tt < nt)
-            *reinterpret_cast<f32x4 *>(&stage[tt][4 * (u % (kFoldSlice / 4))]) = v[r];
+            *reinterpret_cast<f32x4 *>(&stage[tt][4 * (u % (kFoldSlice / 4))]) = fr.v[r];
     }
     if (th < nt) {
-        sm[th] = m;
-        sl[th] = l;
+        sm[th] = fr.m;
+        sl[th] = fr.l;
     }
 }
 
@@ -1023,24 +1041,28 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
     const int d0 = slice * kFoldSlice;
     const int th = threadIdx.x, lane = th & 63, w = th >> 6;
 
-    // first round staged speculatively for min(max_tiles, kFoldTiles) tiles
+    // the first round's loads are issued speculatively for min(max_tiles,
+    // kFoldTiles) tiles, then the row's metadata; the metadata is waited for
+    // (and the workgroup may leave) while the partials are still in flight
     const int nt0 = min(kFoldTiles, a.max_tiles);
-    fold_stage<D>(a, slot0, col, d0, 0, nt0, stage, sm, sl);
-
+    FoldRound fr;
+    fold_load<D>(a, slot0, col, d0, 0, nt0, fr);
     int q0, q_len, seq_len;
     if (!row_ok(a, b, q0, q_len, seq_len))
         return;
     const int ncols = q_len * a.group;
     if (ncols > kSplitCols || col >= ncols)
         return;
+    fold_store(fr, nt0, stage, sm, sl);
     const int n_tiles = (seq_len + G::T - 1) / G::T;
 
     float M = -INFINITY, L = 0.f, acc = 0.f;
     for (int t0 = 0; t0 < n_tiles; t0 += kFoldTiles) {
         const int nt = min(kFoldTiles, n_tiles - t0);
         if (t0 > 0) {
+            fold_load<D>(a, slot0, col, d0, t0, nt, fr);
             __syncthreads();
-            fold_stage<D>(a, slot0, col, d0, t0, nt, stage, sm, sl);
+            fold_store(fr, nt, stage, sm, sl);
         }
         __syncthreads();
         // running max before each tile: inclusive wave scans, then wave totals

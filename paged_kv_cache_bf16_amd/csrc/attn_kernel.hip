@@ -948,8 +948,15 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
 #pragma unroll
         for (int st = 0; st < G::NKS; ++st)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dl][st], pf[st], acc, 0, 0, 0);
-        if (c < ncols)
-            *reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)) = acc;
+        if (c < ncols) {
+            // head_dim 512: 16 KB of partials per tile (an eighth of the tile's
+            // K/V bytes) stream out during the kernel instead of leaving the
+            // L2 dirty for its end
+            if (D == 512)
+                __builtin_nontemporal_store(acc, reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)));
+            else
+                *reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)) = acc;
+        }
     }
     if (w == 0 && g == 0 && c < ncols) {
         a.ws_m[slot * kSplitCols + c] = mx;

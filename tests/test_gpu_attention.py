@@ -243,9 +243,9 @@ def test_decode_step_many_tokens_falls_back_to_two_launches():
 
 
 def test_decode_long_rows():
-    """Decode rows of 65..157 tiles match the oracle and their prefill rows
-    bitwise."""
-    lens = [8193, 16384, 20000, 129]
+    """Decode rows of 2..235 tiles (the longest folds its partials in two
+    staged rounds) match the oracle and their prefill rows bitwise."""
+    lens = [8193, 16384, 20000, 129, 30000]
     w = wl.random_case(23, lens, lens, 8, 2, 128)
     d = w.decode_view()
     g = GpuCase(d)

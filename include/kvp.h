@@ -196,6 +196,11 @@ int kvp_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
  *                    given (large enough) with num_seqs > 1, rows whose
  *                    q_len * G <= 16 take the split-KV decode path and the
  *                    others the prefill path, in two launches on `stream`.
+ *                    The host cannot see the query lengths, so a batch
+ *                    given a workspace launches the split-KV kernels even
+ *                    when none of its rows is short (they then only read
+ *                    the row metadata); a caller that knows its batch has
+ *                    no short row passes no workspace.
  * Numerics: one fixed arithmetic schedule (KV tiles and their softmax folds
  * at fixed absolute positions), so an output row's bits do not depend on
  * the batch, the other rows, the query count or the kernel chosen: a decode

@@ -475,3 +475,54 @@ def test_random_shape_sweep(seed):
     g, out, _ = _run_and_compare(w, rows=rows, what="random %d" % seed)
     if w.batch > 1 and int(w.max_query_len) * (Hq // Hkv) > 16:
         bitwise(g.run(use_workspace=False), out, "random %d: with vs without workspace" % seed)
+
+
+# ------------------------------------------------------------ score shapes that stress the fold
+
+def _shaped(seed, lens, Hq, Hkv, D, slope, qk_scale=0.5):
+    """Full causal prefills whose scores follow a trend along the key
+    position: dim 0 of every key is slope * position and dim 0 of every query
+    is 4, the other dims N(0, qk_scale^2); V ~ N(0, 1).  With the scale
+    1/sqrt(D), slope = 0.37 raises the running maximum by ~24 log2 units per
+    128-key tile (the state's reference moves on every tile and ACC is
+    rescaled each time); a negative slope leaves the maximum in the first
+    tile (later tiles fold with tiny factors)."""
+    w = wl.random_case(seed, lens, lens, Hq, Hkv, D)
+    pos = np.concatenate([np.arange(L, dtype=np.float32) for L in lens])
+    rng = np.random.default_rng(seed + 100)
+    k = rng.standard_normal((pos.size, Hkv, D), dtype=np.float32) * np.float32(qk_scale)
+    k[:, :, 0] = (slope * pos)[:, None]
+    q = rng.standard_normal(w.q.shape, dtype=np.float32) * np.float32(qk_scale)
+    q[:, :, 0] = 4.0
+    w.k = wl.to_bf16_bits(k)
+    w.q = wl.to_bf16_bits(q)
+    return w
+
+
+@pytest.mark.parametrize("slope,D,Hq,Hkv", [(0.37, 128, 8, 2), (-0.37, 128, 8, 2), (0.37, 512, 16, 2),
+                                            (-0.37, 256, 8, 2)])
+def test_trending_scores(slope, D, Hq, Hkv):
+    """Rising scores (the reference moves and ACC is rescaled on every tile)
+    and falling scores (every later tile folds with a vanishing factor):
+    sampled rows match the oracle, and decode rows equal the prefill's last
+    rows bitwise."""
+    w = _shaped(61, [1500, 700, 129], Hq, Hkv, D, slope)
+    g, full, dec = _prefill_then_decode(w)
+    rows = sample_rows(w, 48)
+    compare(full[rows], oracle_attention(w, oracle_pool(w), rows=rows), "trend %g D%d" % (slope, D))
+    bitwise(dec, full[w.query_start_loc[1:] - 1], "trend %g D%d decode vs prefill" % (slope, D))
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 2), (512, 16, 2)])
+def test_peaked_scores(D, Hq, Hkv):
+    """Q and K ~ N(0, 9) (score spread ~9 natural-log units: nearly one-hot
+    softmax rows), V ~ N(0, 1): sampled rows match the oracle and decode rows
+    equal the prefill's last rows bitwise."""
+    w = wl.random_case(67, [1100, 333], [1100, 333], Hq, Hkv, D)
+    rng = np.random.default_rng(168)
+    w.k = wl.to_bf16_bits(rng.standard_normal((w.k.shape), dtype=np.float32) * np.float32(3.0))
+    w.q = wl.to_bf16_bits(rng.standard_normal((w.q.shape), dtype=np.float32) * np.float32(3.0))
+    g, full, dec = _prefill_then_decode(w)
+    rows = sample_rows(w, 48)
+    compare(full[rows], oracle_attention(w, oracle_pool(w), rows=rows), "peaked D%d" % D)
+    bitwise(dec, full[w.query_start_loc[1:] - 1], "peaked D%d decode vs prefill" % D)

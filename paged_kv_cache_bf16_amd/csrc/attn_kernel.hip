@@ -1160,17 +1160,23 @@ __device__ __forceinline__ int db_load_id(const int32_t *bt_row, int tile)
     return bt_row[tile * 8 + (int)(threadIdx.x >> 6)];
 }
 
-// One 1 KB chunk: global_load_lds_dwordx4 with a 64-bit SGPR base, a per-lane
-// 32-bit offset and the wave's LDS destination in M0.  The instruction's
-// immediate offset would move the LDS destination as well, so it stays 0 and
-// chunk offsets go into the base.  Written as inline assembly so that the
-// compiler's wait-count bookkeeping does not treat every later LDS read as
-// dependent on the transfer (it would wait for all LDS reads at each use);
-// the transfers are waited for explicitly (vmcnt(0) before the tile
-// barrier).  The leading s_nop covers the M0-write hazard.
-__device__ __forceinline__ void db_chunk(const char *base, uint32_t off, uint32_t lds_addr)
+// Four consecutive 1 KB chunks of one page: global_load_lds_dwordx4 with a
+// 64-bit SGPR base, a per-lane 32-bit offset and the wave's LDS destination
+// in M0.  The instruction's immediate offset moves the global source and the
+// LDS destination alike, so the four chunks share one base and one M0 value
+// and the chunk step rides in the offset (no address arithmetic per chunk).
+// Written as inline assembly so that the compiler's wait-count bookkeeping
+// does not treat every later LDS read as dependent on the transfer (it would
+// wait for all LDS reads at each use); the transfers are waited for
+// explicitly (vmcnt before the tile barrier).  The leading s_nop covers the
+// M0-write hazard.
+__device__ __forceinline__ void db_chunks4(const char *base, uint32_t off, uint32_t lds_addr)
 {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %1\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:3072"
                  :
                  : "v"(off), "s"(base), "{m0}"(lds_addr)
                  : "memory");
@@ -1188,9 +1194,7 @@ __device__ __forceinline__ void db_issue_half(char *dst, const AttnArgs &a, cons
     id = (uint32_t)id < nb ? id : 0;                          // ids outside the pool read block 0
     const char *src = reinterpret_cast<const char *>(cache + (int64_t)id * block_stride + (int64_t)kvh * BS * D);
     const uint32_t d0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)(dst + page * G::PAGE);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        db_chunk(src + i * 1024, off, d0 + i * 1024);
+    db_chunks4(src, off, d0);
 }
 
 // Zero V of keys >= seq_len in a staged tile (only the tile holding seq_len - 1
@@ -1305,15 +1309,16 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
         const uint16_t *const cache = is_k ? a.k_cache : a.v_cache;
         const int64_t stride = is_k ? a.k_block_stride : a.v_block_stride;
         const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+        static_assert(CPW % 4 == 0 && CPP % 4 == 0, "runs of four chunks");
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) {
+        for (int i = 0; i < CPW; i += 4) {
             const int ch = wave * CPW + i;
             const int page = ch / CPP, part = ch % CPP;
             int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
             id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
             const char *src = reinterpret_cast<const char *>(cache + (int64_t)id * stride + (int64_t)kvh * BS * D);
             const DbOffsets o = db_offsets(page);
-            db_chunk(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
+            db_chunks4(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
         }
     };
     auto fetch_ids = [&](int tile) {
@@ -1442,8 +1447,9 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     auto issue = [&](int tile) {
         char *const buf = kbuf(tile);
         const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+        static_assert(CPW % 4 == 0 && CPP % 4 == 0, "runs of four chunks");
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) {
+        for (int i = 0; i < CPW; i += 4) {
             const int ch = wave * CPW + i;
             const int page = ch / CPP, part = ch % CPP;
             int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
@@ -1452,8 +1458,8 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             const char *ks = reinterpret_cast<const char *>(a.k_cache + (int64_t)id * a.k_block_stride + hoff);
             const char *vs = reinterpret_cast<const char *>(a.v_cache + (int64_t)id * a.v_block_stride + hoff);
             const DbOffsets o = db_offsets(page);
-            db_chunk(ks + part * 1024, o.k, lds_addr(buf + page * G::PAGE + part * 1024));
-            db_chunk(vs + part * 1024, o.v, lds_addr(buf + HALF + page * G::PAGE + part * 1024));
+            db_chunks4(ks + part * 1024, o.k, lds_addr(buf + page * G::PAGE + part * 1024));
+            db_chunks4(vs + part * 1024, o.v, lds_addr(buf + HALF + page * G::PAGE + part * 1024));
         }
     };
     auto fetch_ids = [&](int tile) {
@@ -1841,15 +1847,16 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
         const uint16_t *const cache = is_k ? a.k_cache : a.v_cache;
         const int64_t stride = is_k ? a.k_block_stride : a.v_block_stride;
         const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+        static_assert(CPW % 4 == 0 && CPP % 4 == 0, "runs of four chunks");
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) {
+        for (int i = 0; i < CPW; i += 4) {
             const int ch = w.wave * CPW + i;
             const int page = ch / CPP, part = ch % CPP;
             int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
             id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
             const char *src = reinterpret_cast<const char *>(cache + (int64_t)id * stride + (int64_t)w.kvh * BS * D);
             const DbOffsets o = db_offsets(page);
-            db_chunk(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
+            db_chunks4(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
         }
     };
     auto fetch_ids = [&](int tile) {
@@ -1992,15 +1999,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
         const uint16_t *const cache = is_k ? a.k_cache : a.v_cache;
         const int64_t stride = is_k ? a.k_block_stride : a.v_block_stride;
         const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+        static_assert(CPW % 4 == 0 && CPP % 4 == 0, "runs of four chunks");
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) {
+        for (int i = 0; i < CPW; i += 4) {
             const int ch = wave * CPW + i;
             const int page = ch / CPP, part = ch % CPP;
             int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
             id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
             const char *src = reinterpret_cast<const char *>(cache + (int64_t)id * stride + (int64_t)kvh * BS * D);
             const DbOffsets o = db_offsets(page);
-            db_chunk(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
+            db_chunks4(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
         }
     };
     auto fetch_ids = [&](int tile) {

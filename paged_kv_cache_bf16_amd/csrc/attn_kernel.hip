@@ -579,13 +579,13 @@ __device__ __forceinline__ bool prefill_softmax_stats(f32x4 (&s)[CB][Geo<D>::NKB
 
 // States whose reference moved are rescaled before P.V adds into them
 // (ACC * 1 is exact, so every column of the wave may take the product).
-template <int D, int CB>
+template <int D, int CB, int NL = 0>
 __device__ __forceinline__ void rescale_states(State<D> (&st)[CB], const FoldF (&f)[CB])
 {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int db = 0; db < Geo<D>::NDB; ++db)
+        for (int db = 0; db < Geo<D>::NDB - NL; ++db)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 st[cb].acc[db][i] = __fmul_rn(st[cb].acc[db][i], f[cb].gs);
@@ -603,10 +603,11 @@ __device__ __forceinline__ void prefill_softmax(f32x4 (&s)[CB][Geo<D>::NKB], con
 // P.V with DG 16-dim blocks in flight at once (independent MFMA chains for
 // waves that have their SIMD to themselves): per block the same chain (32-key
 // steps ascending from zero) and the same fold fma(tile, h, ACC) as
-// prefill_pv.
-template <int D, int CB, int DG>
+// prefill_pv.  The last NL dim blocks of ACC (CB == 1) live in LDS at accl
+// (block k of lane L at accl[64 k + L]) instead of registers.
+template <int D, int CB, int DG, int NL = 0>
 __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS],
-                                               const FoldF (&f)[CB], State<D> (&st)[CB])
+                                               const FoldF (&f)[CB], State<D> (&st)[CB], f32x4 *accl = nullptr)
 {
     using G = Geo<D>;
     static_assert(G::NDB % DG == 0, "whole groups");
@@ -651,10 +652,21 @@ __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int d = 0; d < DG; ++d)
+            for (int d = 0; d < DG; ++d) {
+                const int db = db0 + d;
+                if (db >= G::NDB - NL) {
+                    f32x4 *p = accl + (db - (G::NDB - NL)) * 64 + lane;
+                    f32x4 x = *p;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    st[cb].acc[db0 + d][i] = __builtin_fmaf(o[cb][d][i], f[cb].h, st[cb].acc[db0 + d][i]);
+                    for (int i = 0; i < 4; ++i)
+                        x[i] = __builtin_fmaf(o[cb][d][i], f[cb].h, x[i]);
+                    *p = x;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        st[cb].acc[db][i] = __builtin_fmaf(o[cb][d][i], f[cb].h, st[cb].acc[db][i]);
+                }
+            }
     }
 }
 
@@ -1231,11 +1243,15 @@ __device__ __forceinline__ void wait_vm()
 __device__ __forceinline__ void id_dma(const int32_t *src, int npages, uint32_t lds_addr)
 {
     if ((int)(threadIdx.x & 63) < npages)
-        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1"
                      :
-                     : "v"(src + (threadIdx.x & 63)), "{m0}"(lds_addr)
+                     : "v"((uint32_t)(threadIdx.x & 63) * 4u), "s"(src), "{m0}"(lds_addr)
                      : "memory");
 }
+
+// ACC dim blocks per wave that prefill_sb_kernel keeps in LDS (3 KB each per
+// wave: the LDS left beside the K and V tiles at head_dim 512).
+constexpr int sb_acc_blocks_in_lds(int D, int CB) { return CB == 1 && D == 512 ? 3 : 0; }
 
 // Workgroup = (column group, kv head, sequence): NWV waves x CB column
 // blocks.  One LDS buffer for the K tile and one for the V tile, each
@@ -1259,6 +1275,13 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     char *const kbuf = lds;
     char *const vbuf = lds + HALF;
     int32_t *const ids = reinterpret_cast<int32_t *>(lds + 2 * HALF);     // [2][NKB]
+    // head_dim 512: the last NL dim blocks of each wave's ACC live in LDS.
+    // ACC, Q and the tile step's operands otherwise exceed the 256 registers
+    // of a wave, and a spilled value's reload waits (vmcnt) for every K/V
+    // transfer issued before it, which would take the transfers' overlap away.
+    constexpr int NL = sb_acc_blocks_in_lds(D, CB);
+    static_assert(NL == 0 || CB == 1, "LDS-resident ACC blocks for one column block per wave");
+    f32x4 *const accl = reinterpret_cast<f32x4 *>(lds + 2 * HALF + 2 * G::NKB * 4) + (threadIdx.x >> 6) * NL * 64;
 
     const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
     const int per = (n + 7) / 8;
@@ -1294,6 +1317,9 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
         state_init<D>(st[cb]);
         active |= (cg * NCOL + (wave * CB + cb) * 16) < ncols;
     }
+#pragma unroll
+    for (int k = 0; k < NL; ++k)
+        accl[k * 64 + (threadIdx.x & 63)] = f32x4{0.f, 0.f, 0.f, 0.f};
     int min_lim = 0x7fffffff;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
@@ -1348,10 +1374,22 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
         if (t < last)
             issue(true, t + 1);
         if (active) {
+            bool up;
             if ((t + 1) * G::T > min_lim)
-                prefill_softmax<D, CB, true>(sc, cols, t, a.scale_log2, st, pf, f);
+                up = prefill_softmax_stats<D, CB, true>(sc, cols, t, a.scale_log2, st, pf, f);
             else
-                prefill_softmax<D, CB, false>(sc, cols, t, a.scale_log2, st, pf, f);
+                up = prefill_softmax_stats<D, CB, false>(sc, cols, t, a.scale_log2, st, pf, f);
+            if (up) {
+                rescale_states<D, CB, NL>(st, f);
+#pragma unroll
+                for (int k = 0; k < NL; ++k) {
+                    f32x4 x = accl[k * 64 + (threadIdx.x & 63)];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        x[i] = __fmul_rn(x[i], f[0].gs);
+                    accl[k * 64 + (threadIdx.x & 63)] = x;
+                }
+            }
         }
         // V(t) (issued before K(t+1)) has landed
         if (t < last)
@@ -1363,8 +1401,12 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             db_mask_tail<D, NWV>(vbuf, seq_len, t);
             __syncthreads();
         }
-        if (active)
-            tile_pv<D, CB>(vbuf, pf, f, st);
+        if (active) {
+            if constexpr (NL > 0)
+                prefill_pv_grp<D, CB, 4, NL>(vbuf, pf, f, st, accl);
+            else
+                tile_pv<D, CB>(vbuf, pf, f, st);
+        }
         __syncthreads();                                   // V(t) read by every wave
         if (t < last) {
             if (t + 2 <= last)
@@ -1375,6 +1417,9 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             __syncthreads();
         }
     }
+#pragma unroll
+    for (int k = 0; k < NL; ++k)
+        st[0].acc[G::NDB - NL + k] = accl[k * 64 + (threadIdx.x & 63)];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const ColInfo cj = col_info(a, cg * NCOL + (wave * CB + cb) * 16 + c, kvh, q0, q_len, seq_len);
@@ -2282,7 +2327,8 @@ template <int D, int CB, int NWV, int WPE>
 static hipError_t prefill_sb_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
 {
     constexpr int NCOL = NWV * CB * 16;
-    constexpr int LDS_BYTES = Geo<D>::LDS + 2 * Geo<D>::NKB * 4;
+    constexpr int LDS_BYTES = Geo<D>::LDS + 2 * Geo<D>::NKB * 4 + sb_acc_blocks_in_lds(D, CB) * 1024 * NWV;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
     const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;
     const int64_t grid = (n + 7) / 8 * 8;

@@ -605,7 +605,7 @@ __device__ __forceinline__ void prefill_softmax(f32x4 (&s)[CB][Geo<D>::NKB], con
 // steps ascending from zero) and the same fold fma(tile, h, ACC) as
 // prefill_pv.  The last NL dim blocks of ACC (CB == 1) live in LDS at accl
 // (block k of lane L at accl[64 k + L]) instead of registers.
-template <int D, int CB, int DG, int NL = 0>
+template <int D, int CB, int DG, int NL = 0, bool RS = false>
 __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS],
                                                const FoldF (&f)[CB], State<D> (&st)[CB], f32x4 *accl = nullptr)
 {
@@ -664,7 +664,8 @@ __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        st[cb].acc[db][i] = __builtin_fmaf(o[cb][d][i], f[cb].h, st[cb].acc[db][i]);
+                        st[cb].acc[db][i] = __builtin_fmaf(o[cb][d][i], f[cb].h,
+                                                           RS ? __fmul_rn(st[cb].acc[db][i], f[cb].gs) : st[cb].acc[db][i]);
                 }
             }
     }
@@ -1969,16 +1970,17 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
 // t, folds (R, L) and hands the fold factors and P^T to its consumer (waves
 // 4-7) through LDS; the consumer runs P.V of tile t-1 and folds it into ACC
 // at the same time.  Both roles use the tile-step functions of the other
-// kernels unchanged, so the bits are the same; the two waves of a SIMD are a
-// stage apart, so one's MFMAs fill the other's softmax.  K and V tiles have
-// two LDS buffers each (K(t+1) and V(t) load while K(t) and V(t-1) are read),
-// two barriers per tile.  64 columns per workgroup, for grids that leave
-// CUs idle with more columns per workgroup.
+// kernels, so the bits are the same (the consumer takes ACC * gs inside its
+// fold on every tile: gs is 1 unless the reference moved, and ACC * 1 is
+// exact); the two waves of a SIMD are a stage apart, so one's MFMAs fill the
+// other's softmax.  K and V tiles have two LDS buffers each (K(t+1) and V(t)
+// load while K(t) and V(t-1) are read), two barriers per tile.  64 columns
+// per workgroup, for grids that leave CUs idle with more columns per
+// workgroup.
 template <int D>
 struct StageX {
     bf16x8 p[Geo<D>::NKS][64];
     float gs[64], h[64], R[64], L[64];
-    int up;
 };
 
 template <int D, int WPE>
@@ -2071,8 +2073,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // step t: the producer computes tile t, the consumer tile t - 1
-    for (int t = 0; t <= last + 1; ++t) {
+    // step t: the producer computes tile t, the consumer tile t - 1.  Each
+    // role runs its own copy of the step loop, with the same barriers in the
+    // same order, so the two roles' values never meet at a join.
+    auto step_head = [&](int t) {
         // K(t+1) and V(t) go into buffers last read in step t - 1
         if (t + 1 <= last)
             issue(true, t + 1);
@@ -2083,53 +2087,65 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
             db_mask_tail<D, NWV>(stage(t - 1) + HALF, seq_len, t - 1);
             __syncthreads();
         }
-        bf16x8 pf[1][G::NKS];
-        FoldF f[1];
-        bool any_up = false;
-        if (producer) {
-            if (active && t <= last) {
+    };
+    if (producer) {
+        for (int t = 0; t <= last + 1; ++t) {
+            step_head(t);
+            const bool work = active && t <= last;
+            bf16x8 pf[1][G::NKS];
+            FoldF f[1];
+            if (work) {
                 f32x4 sc[1][G::NKB];
                 tile_qk<D, 1>(stage(t), cols, sc);
                 if ((t + 1) * G::T > min_lim)
-                    any_up = prefill_softmax_stats<D, 1, true>(sc, cols, t, a.scale_log2, st, pf, f);
+                    prefill_softmax_stats<D, 1, true>(sc, cols, t, a.scale_log2, st, pf, f);
                 else
-                    any_up = prefill_softmax_stats<D, 1, false>(sc, cols, t, a.scale_log2, st, pf, f);
+                    prefill_softmax_stats<D, 1, false>(sc, cols, t, a.scale_log2, st, pf, f);
             }
-        } else if (active && t >= 1) {
+            __syncthreads();                               // the consumer is done with the hand-off of t - 1
+            if (t + 2 <= last)
+                fetch_ids(t + 2);                          // its slot held the ids of V(t), issued above
+            if (work) {
 #pragma unroll
-            for (int stp = 0; stp < G::NKS; ++stp)
-                pf[0][stp] = x.p[stp][lane];
-            f[0].gs = x.gs[lane];
-            f[0].h = x.h[lane];
-            if (x.up)
-                rescale_states<D, 1>(st, f);
-            tile_pv<D, 1>(stage(t - 1) + HALF, pf, f, st);
-        }
-        __syncthreads();                                   // the consumer is done with the hand-off of t - 1
-        if (t + 2 <= last)
-            fetch_ids(t + 2);                              // its slot held the ids of V(t), issued above
-        if (producer && active && t <= last) {
-#pragma unroll
-            for (int stp = 0; stp < G::NKS; ++stp)
-                x.p[stp][lane] = pf[0][stp];
-            x.gs[lane] = f[0].gs;
-            x.h[lane] = f[0].h;
-            if (lane == 0)
-                x.up = any_up ? 1 : 0;
-            if (t == last) {
-                x.R[lane] = st[0].R;
-                x.L[lane] = st[0].L;
+                for (int stp = 0; stp < G::NKS; ++stp)
+                    x.p[stp][lane] = pf[0][stp];
+                x.gs[lane] = f[0].gs;
+                x.h[lane] = f[0].h;
+                if (t == last) {
+                    x.R[lane] = st[0].R;
+                    x.L[lane] = st[0].L;
+                }
+            }
+            if (t <= last) {
+                __builtin_amdgcn_s_waitcnt(0);             // K(t+1), V(t), ids(t+2) landed
+                __syncthreads();                           // and the hand-off of t is visible
             }
         }
-        if (t <= last) {
-            __builtin_amdgcn_s_waitcnt(0);                 // K(t+1), V(t), ids(t+2) landed
-            __syncthreads();                               // and the hand-off of t is visible
+    } else {
+        for (int t = 0; t <= last + 1; ++t) {
+            step_head(t);
+            if (active && t >= 1) {
+                bf16x8 pf[1][G::NKS];
+                FoldF f[1];
+#pragma unroll
+                for (int stp = 0; stp < G::NKS; ++stp)
+                    pf[0][stp] = x.p[stp][lane];
+                f[0].gs = x.gs[lane];
+                f[0].h = x.h[lane];
+                // ACC * gs inside the fold, for every tile (ACC * 1 is exact)
+                prefill_pv_grp<D, 1, (D == 128 ? 8 : 4), 0, true>(stage(t - 1) + HALF, pf, f, st);
+            }
+            __syncthreads();                               // done with the hand-off of t - 1
+            if (t <= last) {
+                __builtin_amdgcn_s_waitcnt(0);             // K(t+1), V(t) landed
+                __syncthreads();                           // and the hand-off of t is visible
+            }
         }
-    }
-    if (!producer && ci.lim > 0) {
-        st[0].R = x.R[lane];
-        st[0].L = x.L[lane];
-        store_out<D>(a, ci, st[0]);
+        if (ci.lim > 0) {
+            st[0].R = x.R[lane];
+            st[0].L = x.L[lane];
+            store_out<D>(a, ci, st[0]);
+        }
     }
 }
 

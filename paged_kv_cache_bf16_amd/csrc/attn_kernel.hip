@@ -977,7 +977,7 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     }
 }
 
-// Fold kernel.  Workgroup = (64 consecutive dims of one column, kv head,
+// Fold kernel.  Workgroup = (32 consecutive dims of one column, kv head,
 // sequence).  All waves stage the column's per-tile partials into LDS, with
 // every load of a round issued before any is used (the first round is
 // fetched before the row's length is even known: the workspace holds
@@ -985,14 +985,14 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
 // max before t -- the max of the earlier tile maxima, exact in any order,
 // whose reference is the state's reference -- so all factors come from one
 // prefix-max scan, stored per tile as one (gs, h) pair; then wave 0 runs
-// the dependent ACC chain (one dim per lane) and wave 1 the L chain, each in
+// the dependent ACC chain (one dim per lane, half the wave) and wave 1 the L chain, each in
 // ascending tile order, and wave 0 writes the BF16 output.
-constexpr int kFoldSlice = 64;
+constexpr int kFoldSlice = 32;
 constexpr int kFoldTiles = 192;
 constexpr int kFoldUnits = kFoldTiles * (kFoldSlice / 4) / NT;   // 16-byte loads per thread per round
 
 // One round of the fold's inputs: the (acc, m, l) partials of tiles
-// t0 .. t0+nt-1 for one column and one 64-dim slice.  fold_load issues the
+// t0 .. t0+nt-1 for one column and one 32-dim slice.  fold_load issues the
 // loads (rounds of whole workgroups past the last tile issue none);
 // fold_store waits for them and writes them to LDS.
 struct FoldRound {
@@ -1110,7 +1110,7 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
         __syncthreads();
         // wave 0 folds ACC (one dim per lane), wave 1 folds L, side by side;
         // every thread carries M (the next round's scan starts from it)
-        if (w == 0) {
+        if (w == 0 && th < kFoldSlice) {
 #pragma unroll 8
             for (int tt = 0; tt < nt; ++tt) {
                 const float2 gh = sgh[tt];
@@ -2484,7 +2484,7 @@ static hipError_t split_launch(const AttnArgs &a, int max_query_len, hipStream_t
         hipLaunchKernelGGL((split_partial_kernel<D, true>), dim3(grid.x + 1, grid.y, grid.z), dim3(NT), 0, s, a);
     else
         hipLaunchKernelGGL((split_partial_kernel<D, false>), grid, dim3(NT), 0, s, a);
-    // one fold workgroup per (column that can exist, 64-dim slice)
+    // one fold workgroup per (column that can exist, 32-dim slice)
     const int max_cols = min(kSplitCols, max_query_len * a.group);
     const dim3 fgrid((unsigned)(max_cols * (D / kFoldSlice)), (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     hipLaunchKernelGGL((split_fold_kernel<D>), fgrid, dim3(NT), 0, s, a);

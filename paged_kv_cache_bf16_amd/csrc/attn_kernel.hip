@@ -74,9 +74,18 @@ __device__ __forceinline__ int ksw(int tok, int page)
     return tok ^ ((((tok >> 3) ^ page) & 1) << 2);
 }
 
-__device__ __forceinline__ int vsw(int half, int d)
+// LDS slot (16-byte unit) of V unit (dim d, token half) inside a staged page:
+// each 1 KB chunk holds 32 dims, half 0 of all 32 then half 1, so the 16
+// lanes of one P.V operand read (16 consecutive dims, one half) touch 256
+// contiguous bytes (no bank conflicts), and chunk i of the page still comes
+// from source bytes [i KB, (i+1) KB) of the pool's [Dh][16 tokens] page.
+// VH = false selects the earlier order (the two halves of a dim adjacent,
+// swapped on alternate 4-dim groups), whose reads conflict in the LDS banks
+// but leaves the Dh 512 single-buffer kernel within its registers.
+template <bool VH = true>
+__device__ __forceinline__ int vslot(int d, int half)
 {
-    return half ^ (((d >> 2) ^ (d >> 3)) & 1);
+    return VH ? (d >> 5) * 64 + half * 32 + (d & 31) : d * 2 + (half ^ (((d >> 2) ^ (d >> 3)) & 1));
 }
 
 // IEEE 754-2019 maximum (v_maximum3_f32 for nested uses; unlike fmaxf it
@@ -341,7 +350,7 @@ __device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB
     const int g = lane >> 4, c = lane & 15;
     auto vaddr = [&](int db) -> const char * {
         const int d = 16 * db + c;
-        return vl + (g >> 1) * G::PAGE + (d * 2 + vsw(g & 1, d)) * 16;
+        return vl + (g >> 1) * G::PAGE + vslot<>(d, g & 1) * 16;
     };
     bf16x8 vf[G::NKS], vn[G::NKS];
     {
@@ -605,7 +614,7 @@ __device__ __forceinline__ void prefill_softmax(f32x4 (&s)[CB][Geo<D>::NKB], con
 // steps ascending from zero) and the same fold fma(tile, h, ACC) as
 // prefill_pv.  The last NL dim blocks of ACC (CB == 1) live in LDS at accl
 // (block k of lane L at accl[64 k + L]) instead of registers.
-template <int D, int CB, int DG, int NL = 0, bool RS = false>
+template <int D, int CB, int DG, int NL = 0, bool RS = false, bool VH = true>
 __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS],
                                                const FoldF (&f)[CB], State<D> (&st)[CB], f32x4 *accl = nullptr)
 {
@@ -615,7 +624,7 @@ __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf
     const int g = lane >> 4, c = lane & 15;
     auto vaddr = [&](int db, int stp) -> const char * {
         const int d = 16 * db + c;
-        return vl + (g >> 1) * G::PAGE + (d * 2 + vsw(g & 1, d)) * 16 + 2 * stp * G::PAGE;
+        return vl + (g >> 1) * G::PAGE + vslot<VH>(d, g & 1) * 16 + 2 * stp * G::PAGE;
     };
 #pragma unroll
     for (int db0 = 0; db0 < G::NDB; db0 += DG) {
@@ -1149,20 +1158,25 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
 
 // Per-lane source byte offsets (inside one page) of the 16-byte units that
 // chunk 0 of page `page` holds at this lane's LDS slots; chunk i adds i KB
-// (the swizzles of K and V do not depend on the chunk).
+// (the K swizzle and the V slot order do not depend on the chunk).
 struct DbOffsets {
     uint32_t k, v;
 };
 
+template <bool VH = true>
 __device__ __forceinline__ DbOffsets db_offsets(int page)
 {
     const int lane = threadIdx.x & 63;
     DbOffsets o;
     // K: slot (du, tok') holds unit (du, ksw(tok', page))
     o.k = (uint32_t)(((lane >> 4) * 16 + ksw(lane & 15, page)) * 16);
-    // V: slot (d, half') holds unit (d, vsw(half', d))
-    const int d = lane >> 1;
-    o.v = (uint32_t)((d * 2 + vsw(lane & 1, d)) * 16);
+    // V: slot vslot(d, half) holds unit (d, half), at source byte 32 d + 16 half
+    if (VH) {
+        o.v = (uint32_t)((lane & 31) * 32 + (lane >> 5) * 16);
+    } else {
+        const int d = lane >> 1;
+        o.v = (uint32_t)((d * 2 + ((lane & 1) ^ (((d >> 2) ^ (d >> 3)) & 1))) * 16);
+    }
     return o;
 }
 
@@ -1212,7 +1226,7 @@ __device__ __forceinline__ void db_issue_half(char *dst, const AttnArgs &a, cons
 
 // Zero V of keys >= seq_len in a staged tile (only the tile holding seq_len - 1
 // and later ones can have such keys).
-template <int D, int NWV>
+template <int D, int NWV, bool VH = true>
 __device__ __forceinline__ void db_mask_tail(char *vl, int seq_len, int tile)
 {
     using G = Geo<D>;
@@ -1222,7 +1236,8 @@ __device__ __forceinline__ void db_mask_tail(char *vl, int seq_len, int tile)
         const int valid = seq_len - (tile * G::NKB + pg) * BS;
         if (valid >= BS)
             continue;
-        const int d = slot >> 1, hf = vsw(slot & 1, d);
+        const int d = slot >> 1;
+        const int hf = VH ? (slot >> 5) & 1 : (slot & 1) ^ (((d >> 2) ^ (d >> 3)) & 1);   // the slot's token half
         u32x4 *q = reinterpret_cast<u32x4 *>(vl + pg * G::PAGE + slot * 16);
         *q = mask_tokens(*q, hf * 8, valid);
     }
@@ -1344,7 +1359,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
             id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
             const char *src = reinterpret_cast<const char *>(cache + (int64_t)id * stride + (int64_t)kvh * BS * D);
-            const DbOffsets o = db_offsets(page);
+            const DbOffsets o = db_offsets<false>(page);
             db_chunks4(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
         }
     };
@@ -1399,15 +1414,11 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             wait_vm<0>();
         __syncthreads();
         if ((t + 1) * G::T > seq_len) {
-            db_mask_tail<D, NWV>(vbuf, seq_len, t);
+            db_mask_tail<D, NWV, false>(vbuf, seq_len, t);
             __syncthreads();
         }
-        if (active) {
-            if constexpr (NL > 0)
-                prefill_pv_grp<D, CB, 4, NL>(vbuf, pf, f, st, accl);
-            else
-                tile_pv<D, CB>(vbuf, pf, f, st);
-        }
+        if (active)
+            prefill_pv_grp<D, CB, 4, NL, false, false>(vbuf, pf, f, st, accl);
         __syncthreads();                                   // V(t) read by every wave
         if (t < last) {
             if (t + 2 <= last)
@@ -1744,7 +1755,7 @@ __device__ __forceinline__ void ws_fold_pv(const char *vl, const float (&m)[CB],
     }
     auto vaddr = [&](int db, int stp) -> const char * {
         const int d = 16 * db + c;
-        return vl + (g >> 1) * G::PAGE + (d * 2 + vsw(g & 1, d)) * 16 + 2 * stp * G::PAGE;
+        return vl + (g >> 1) * G::PAGE + vslot<>(d, g & 1) * 16 + 2 * stp * G::PAGE;
     };
 #pragma unroll
     for (int d0 = 0; d0 < HD; d0 += DG) {

@@ -79,13 +79,9 @@ __device__ __forceinline__ int ksw(int tok, int page)
 // lanes of one P.V operand read (16 consecutive dims, one half) touch 256
 // contiguous bytes (no bank conflicts), and chunk i of the page still comes
 // from source bytes [i KB, (i+1) KB) of the pool's [Dh][16 tokens] page.
-// VH = false selects the earlier order (the two halves of a dim adjacent,
-// swapped on alternate 4-dim groups), whose reads conflict in the LDS banks
-// but leaves the Dh 512 single-buffer kernel within its registers.
-template <bool VH = true>
 __device__ __forceinline__ int vslot(int d, int half)
 {
-    return VH ? (d >> 5) * 64 + half * 32 + (d & 31) : d * 2 + (half ^ (((d >> 2) ^ (d >> 3)) & 1));
+    return (d >> 5) * 64 + half * 32 + (d & 31);
 }
 
 // IEEE 754-2019 maximum (v_maximum3_f32 for nested uses; unlike fmaxf it
@@ -350,7 +346,7 @@ __device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB
     const int g = lane >> 4, c = lane & 15;
     auto vaddr = [&](int db) -> const char * {
         const int d = 16 * db + c;
-        return vl + (g >> 1) * G::PAGE + vslot<>(d, g & 1) * 16;
+        return vl + (g >> 1) * G::PAGE + vslot(d, g & 1) * 16;
     };
     bf16x8 vf[G::NKS], vn[G::NKS];
     {
@@ -453,11 +449,12 @@ __device__ __forceinline__ void prefill_qk(const char *kl, const Cols<D> (&cols)
     }
 }
 
-// Phase 1 for wide heads (many 32-dim steps): the same MFMA chains (one per
-// (column block, key block), head dim ascending from zero), walked with the
-// head-dim step outermost so that only one step's K fragments (plus the
-// next step's) are live.
-template <int D, int CB>
+// Phase 1 for wide heads (many 32-dim steps) and single-column-block waves:
+// the same MFMA chains (one per (column block, key block), head dim
+// ascending from zero), walked with the head-dim step outermost; the K
+// fragments are read through a ring of RD register sets, each reloaded
+// with the fragment RD positions ahead as soon as its MFMA is issued.
+template <int D, int CB, int RD = 6>
 __device__ __forceinline__ void prefill_qk_wide(const char *kl, const Cols<D> (&cols)[CB],
                                                 f32x4 (&s)[CB][Geo<D>::NKB])
 {
@@ -474,33 +471,30 @@ __device__ __forceinline__ void prefill_qk_wide(const char *kl, const Cols<D> (&
 #pragma unroll
     for (int kb = 0; kb < G::NKB; ++kb)
         base[kb] = kaddr(kb);
-    bf16x8 kf[G::NKB], kn[G::NKB];
-#pragma unroll
-    for (int kb = 0; kb < G::NKB; ++kb)
-        kf[kb] = *reinterpret_cast<const bf16x8 *>(base[kb]);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int kb = 0; kb < G::NKB; ++kb)
             s[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // fragment j = (dim step j / NKB, key block j % NKB)
+    constexpr int N = G::NDS * G::NKB;
+    static_assert(RD >= 1 && RD <= N, "ring depth");
+    auto frag = [&](int j) { return *reinterpret_cast<const bf16x8 *>(base[j % G::NKB] + (j / G::NKB) * 1024); };
+    bf16x8 ring[RD];
 #pragma unroll
-    for (int ds = 0; ds < G::NDS; ++ds) {
-        if (ds + 1 < G::NDS) {
+    for (int j = 0; j < RD; ++j)
+        ring[j] = frag(j);
 #pragma unroll
-            for (int kb = 0; kb < G::NKB; ++kb)
-                kn[kb] = *reinterpret_cast<const bf16x8 *>(base[kb] + (ds + 1) * 1024);
-        }
+    for (int j = 0; j < N; ++j) {
+        const int ds = j / G::NKB, kb = j % G::NKB;
 #pragma unroll
-        for (int kb = 0; kb < G::NKB; ++kb)
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-                s[cb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], cols[cb].qf[ds], s[cb][kb], 0, 0, 0);
-#pragma unroll
-        for (int kb = 0; kb < G::NKB; ++kb)
-            kf[kb] = kn[kb];
-        if (ds + 1 < G::NDS)
-            __builtin_amdgcn_sched_group_barrier(0x100, G::NKB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, G::NKB * CB, 0);
+        for (int cb = 0; cb < CB; ++cb)
+            s[cb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[j % RD], cols[cb].qf[ds], s[cb][kb], 0, 0, 0);
+        if (j + RD < N)
+            ring[j % RD] = frag(j + RD);
+        __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
+        if (j + RD < N)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -614,7 +608,7 @@ __device__ __forceinline__ void prefill_softmax(f32x4 (&s)[CB][Geo<D>::NKB], con
 // steps ascending from zero) and the same fold fma(tile, h, ACC) as
 // prefill_pv.  The last NL dim blocks of ACC (CB == 1) live in LDS at accl
 // (block k of lane L at accl[64 k + L]) instead of registers.
-template <int D, int CB, int DG, int NL = 0, bool RS = false, bool VH = true>
+template <int D, int CB, int DG, int NL = 0, bool RS = false>
 __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS],
                                                const FoldF (&f)[CB], State<D> (&st)[CB], f32x4 *accl = nullptr)
 {
@@ -624,7 +618,7 @@ __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf
     const int g = lane >> 4, c = lane & 15;
     auto vaddr = [&](int db, int stp) -> const char * {
         const int d = 16 * db + c;
-        return vl + (g >> 1) * G::PAGE + vslot<VH>(d, g & 1) * 16 + 2 * stp * G::PAGE;
+        return vl + (g >> 1) * G::PAGE + vslot(d, g & 1) * 16 + 2 * stp * G::PAGE;
     };
 #pragma unroll
     for (int db0 = 0; db0 < G::NDB; db0 += DG) {
@@ -1163,7 +1157,6 @@ struct DbOffsets {
     uint32_t k, v;
 };
 
-template <bool VH = true>
 __device__ __forceinline__ DbOffsets db_offsets(int page)
 {
     const int lane = threadIdx.x & 63;
@@ -1171,12 +1164,7 @@ __device__ __forceinline__ DbOffsets db_offsets(int page)
     // K: slot (du, tok') holds unit (du, ksw(tok', page))
     o.k = (uint32_t)(((lane >> 4) * 16 + ksw(lane & 15, page)) * 16);
     // V: slot vslot(d, half) holds unit (d, half), at source byte 32 d + 16 half
-    if (VH) {
-        o.v = (uint32_t)((lane & 31) * 32 + (lane >> 5) * 16);
-    } else {
-        const int d = lane >> 1;
-        o.v = (uint32_t)((d * 2 + ((lane & 1) ^ (((d >> 2) ^ (d >> 3)) & 1))) * 16);
-    }
+    o.v = (uint32_t)((lane & 31) * 32 + (lane >> 5) * 16);
     return o;
 }
 
@@ -1226,7 +1214,7 @@ __device__ __forceinline__ void db_issue_half(char *dst, const AttnArgs &a, cons
 
 // Zero V of keys >= seq_len in a staged tile (only the tile holding seq_len - 1
 // and later ones can have such keys).
-template <int D, int NWV, bool VH = true>
+template <int D, int NWV>
 __device__ __forceinline__ void db_mask_tail(char *vl, int seq_len, int tile)
 {
     using G = Geo<D>;
@@ -1236,8 +1224,7 @@ __device__ __forceinline__ void db_mask_tail(char *vl, int seq_len, int tile)
         const int valid = seq_len - (tile * G::NKB + pg) * BS;
         if (valid >= BS)
             continue;
-        const int d = slot >> 1;
-        const int hf = VH ? (slot >> 5) & 1 : (slot & 1) ^ (((d >> 2) ^ (d >> 3)) & 1);   // the slot's token half
+        const int hf = (slot >> 5) & 1;                 // the slot's token half (vslot)
         u32x4 *q = reinterpret_cast<u32x4 *>(vl + pg * G::PAGE + slot * 16);
         *q = mask_tokens(*q, hf * 8, valid);
     }
@@ -1359,7 +1346,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
             id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
             const char *src = reinterpret_cast<const char *>(cache + (int64_t)id * stride + (int64_t)kvh * BS * D);
-            const DbOffsets o = db_offsets<false>(page);
+            const DbOffsets o = db_offsets(page);
             db_chunks4(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
         }
     };
@@ -1383,9 +1370,8 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
         f32x4 sc[CB][G::NKB];
         bf16x8 pf[CB][G::NKS];
         FoldF f[CB];
-        if (active) {
-            tile_qk<D, CB>(kbuf, cols, sc);
-        }
+        if (active)
+            prefill_qk_wide<D, CB, 4>(kbuf, cols, sc);      // a shallow ring: registers are scarce here
         __syncthreads();                                   // K(t) read by every wave
         if (t < last)
             issue(true, t + 1);
@@ -1414,11 +1400,11 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             wait_vm<0>();
         __syncthreads();
         if ((t + 1) * G::T > seq_len) {
-            db_mask_tail<D, NWV, false>(vbuf, seq_len, t);
+            db_mask_tail<D, NWV>(vbuf, seq_len, t);
             __syncthreads();
         }
         if (active)
-            prefill_pv_grp<D, CB, 4, NL, false, false>(vbuf, pf, f, st, accl);
+            prefill_pv_grp<D, CB, 2, NL>(vbuf, pf, f, st, accl);
         __syncthreads();                                   // V(t) read by every wave
         if (t < last) {
             if (t + 2 <= last)
@@ -1755,7 +1741,7 @@ __device__ __forceinline__ void ws_fold_pv(const char *vl, const float (&m)[CB],
     }
     auto vaddr = [&](int db, int stp) -> const char * {
         const int d = 16 * db + c;
-        return vl + (g >> 1) * G::PAGE + vslot<>(d, g & 1) * 16 + 2 * stp * G::PAGE;
+        return vl + (g >> 1) * G::PAGE + vslot(d, g & 1) * 16 + 2 * stp * G::PAGE;
     };
 #pragma unroll
     for (int d0 = 0; d0 < HD; d0 += DG) {

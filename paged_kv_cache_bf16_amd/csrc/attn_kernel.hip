@@ -1582,7 +1582,7 @@ struct PairX {
     bf16x8 p[CB][Geo<D>::NKS][64];
 };
 
-template <int D, int CB>
+template <int D, int CB, int RD = 6>
 __device__ __forceinline__ void ws_qk(const char *kl, const Cols<D> (&cols)[CB], f32x4 (&s)[CB][Geo<D>::NKB / 2],
                                       int h)
 {
@@ -1599,32 +1599,29 @@ __device__ __forceinline__ void ws_qk(const char *kl, const Cols<D> (&cols)[CB],
         const int tok = ((c >> 2) & 1) * 8 + e * 4 + (c & 3);
         base[k] = kl + page * G::PAGE + ksw(tok, page) * 16 + g * 256;
     }
-    bf16x8 kf[HK], kn[HK];
 #pragma unroll
-    for (int k = 0; k < HK; ++k) {
-        kf[k] = *reinterpret_cast<const bf16x8 *>(base[k]);
+    for (int k = 0; k < HK; ++k)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
             s[cb][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    // fragment j = (dim step j / HK, key block j % HK), RD of them in flight
+    constexpr int N = G::NDS * HK;
+    auto frag = [&](int j) { return *reinterpret_cast<const bf16x8 *>(base[j % HK] + (j / HK) * 1024); };
+    bf16x8 ring[RD];
 #pragma unroll
-    for (int ds = 0; ds < G::NDS; ++ds) {
-        if (ds + 1 < G::NDS) {
+    for (int j = 0; j < RD; ++j)
+        ring[j] = frag(j);
 #pragma unroll
-            for (int k = 0; k < HK; ++k)
-                kn[k] = *reinterpret_cast<const bf16x8 *>(base[k] + (ds + 1) * 1024);
-        }
+    for (int j = 0; j < N; ++j) {
+        const int ds = j / HK, k = j % HK;
 #pragma unroll
-        for (int k = 0; k < HK; ++k)
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-                s[cb][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k], cols[cb].qf[ds], s[cb][k], 0, 0, 0);
-#pragma unroll
-        for (int k = 0; k < HK; ++k)
-            kf[k] = kn[k];
-        if (ds + 1 < G::NDS)
-            __builtin_amdgcn_sched_group_barrier(0x100, HK, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, HK * CB, 0);
+        for (int cb = 0; cb < CB; ++cb)
+            s[cb][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[j % RD], cols[cb].qf[ds], s[cb][k], 0, 0, 0);
+        if (j + RD < N)
+            ring[j % RD] = frag(j + RD);
+        __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
+        if (j + RD < N)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
 }

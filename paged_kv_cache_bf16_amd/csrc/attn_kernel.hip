@@ -2443,9 +2443,9 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
     // with 128 columns if that does, else the producer / consumer kernel (64
     // columns, twice the workgroups).  Dh 256: double-buffered or producer /
     // consumer by the same rule.  Dh 512 (one K and one V buffer; a
-    // double-buffered tile would not fit in LDS): 128 columns per workgroup
-    // from two workgroups per CU on (fewer re-reads of the pages), else the
-    // wave-pair kernel.
+    // double-buffered tile would not fit in LDS): the single-buffer kernel
+    // with 128 columns per workgroup when that yields a workgroup per CU,
+    // else the wave-pair kernel (64 columns).
     const int64_t rows = (int64_t)a.num_seqs * a.num_kv_heads;
     const int64_t groups256 = rows * ((mq * a.group + 255) / 256);
     const int64_t groups128 = rows * ((mq * a.group + 127) / 128);
@@ -2461,7 +2461,7 @@ hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hi
             return prefill_db_launch<256, 1, 8, 2>(a, s, blocks, mq);
         return prefill_ss_launch<256, 2>(a, s, blocks, mq);
     case 512:
-        if (groups128 >= 512)
+        if (groups128 >= 256)
             return prefill_sb_launch<512, 1, 8, 2>(a, s, blocks, mq);
         return prefill_ws_launch<512, 8, 2, 1>(a, s, blocks, mq);
     default: return hipErrorInvalidValue;

@@ -432,7 +432,8 @@ def test_fused_qkv_view_decode_step():
     ([300, 133], 32, 8, 128, 64),        # few columns: producer / consumer kernel, 64 columns per workgroup
     ([20, 45], 8, 2, 256, 64),           # the same at head_dim 256
     ([900], 16, 2, 512, 64),             # head_dim 512, small grid: wave-pair kernel
-], ids=["db128", "db256", "ss128", "ss256", "ws512"])
+    ([2100], 16, 2, 512, 128),           # 264 workgroups of 128 columns: prefill_sb_kernel<512>
+], ids=["db128", "db256", "ss128", "ss256", "ws512", "sb512"])
 def test_prefill_kernel_per_grid_size(lens, Hq, Hkv, D, ncol):
     """Each prefill kernel the launcher picks by grid size (identified by its
     workgroup count) against the oracle on sampled rows, and every row's

@@ -1245,10 +1245,13 @@ __device__ __forceinline__ void wait_vm()
 // transfers, so that no compiler-inserted wait stalls on the transfers.
 __device__ __forceinline__ void id_dma(const int32_t *src, int npages, uint32_t lds_addr)
 {
-    if ((int)(threadIdx.x & 63) < npages)
+    // lane index from mbcnt (computed here rather than kept live from the
+    // work-item id, which the tile loops would otherwise hold or spill)
+    const uint32_t ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    if ((int)ln < npages)
         asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1"
                      :
-                     : "v"((uint32_t)(threadIdx.x & 63) * 4u), "s"(src), "{m0}"(lds_addr)
+                     : "v"(ln * 4u), "s"(src), "{m0}"(lds_addr)
                      : "memory");
 }
 

@@ -582,13 +582,13 @@ __device__ __forceinline__ bool prefill_softmax_stats(f32x4 (&s)[CB][Geo<D>::NKB
 
 // States whose reference moved are rescaled before P.V adds into them
 // (ACC * 1 is exact, so every column of the wave may take the product).
-template <int D, int CB, int NL = 0>
+template <int D, int CB>
 __device__ __forceinline__ void rescale_states(State<D> (&st)[CB], const FoldF (&f)[CB])
 {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int db = 0; db < Geo<D>::NDB - NL; ++db)
+        for (int db = 0; db < Geo<D>::NDB; ++db)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 st[cb].acc[db][i] = __fmul_rn(st[cb].acc[db][i], f[cb].gs);
@@ -606,11 +606,10 @@ __device__ __forceinline__ void prefill_softmax(f32x4 (&s)[CB][Geo<D>::NKB], con
 // P.V with DG 16-dim blocks in flight at once (independent MFMA chains for
 // waves that have their SIMD to themselves): per block the same chain (32-key
 // steps ascending from zero) and the same fold fma(tile, h, ACC) as
-// prefill_pv.  The last NL dim blocks of ACC (CB == 1) live in LDS at accl
-// (block k of lane L at accl[64 k + L]) instead of registers.
-template <int D, int CB, int DG, int NL = 0, bool RS = false>
+// prefill_pv.
+template <int D, int CB, int DG, bool RS = false>
 __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS],
-                                               const FoldF (&f)[CB], State<D> (&st)[CB], f32x4 *accl = nullptr)
+                                               const FoldF (&f)[CB], State<D> (&st)[CB])
 {
     using G = Geo<D>;
     static_assert(G::NDB % DG == 0, "whole groups");
@@ -655,22 +654,12 @@ __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-            for (int d = 0; d < DG; ++d) {
-                const int db = db0 + d;
-                if (db >= G::NDB - NL) {
-                    f32x4 *p = accl + (db - (G::NDB - NL)) * 64 + lane;
-                    f32x4 x = *p;
+            for (int d = 0; d < DG; ++d)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        x[i] = __builtin_fmaf(o[cb][d][i], f[cb].h, x[i]);
-                    *p = x;
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        st[cb].acc[db][i] = __builtin_fmaf(o[cb][d][i], f[cb].h,
-                                                           RS ? __fmul_rn(st[cb].acc[db][i], f[cb].gs) : st[cb].acc[db][i]);
-                }
-            }
+                for (int i = 0; i < 4; ++i)
+                    st[cb].acc[db0 + d][i] = __builtin_fmaf(o[cb][d][i], f[cb].h,
+                                                            RS ? __fmul_rn(st[cb].acc[db0 + d][i], f[cb].gs)
+                                                               : st[cb].acc[db0 + d][i]);
     }
 }
 
@@ -1255,10 +1244,6 @@ __device__ __forceinline__ void id_dma(const int32_t *src, int npages, uint32_t 
                      : "memory");
 }
 
-// ACC dim blocks per wave that prefill_sb_kernel keeps in LDS (3 KB each per
-// wave: the LDS left beside the K and V tiles at head_dim 512).
-constexpr int sb_acc_blocks_in_lds(int D, int CB) { return CB == 1 && D == 512 ? 3 : 0; }
-
 // Workgroup = (column group, kv head, sequence): NWV waves x CB column
 // blocks.  One LDS buffer for the K tile and one for the V tile, each
 // refilled straight from HBM as soon as its last reader is done: K(t+1) is in
@@ -1281,13 +1266,6 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     char *const kbuf = lds;
     char *const vbuf = lds + HALF;
     int32_t *const ids = reinterpret_cast<int32_t *>(lds + 2 * HALF);     // [2][NKB]
-    // head_dim 512: the last NL dim blocks of each wave's ACC live in LDS.
-    // ACC, Q and the tile step's operands otherwise exceed the 256 registers
-    // of a wave, and a spilled value's reload waits (vmcnt) for every K/V
-    // transfer issued before it, which would take the transfers' overlap away.
-    constexpr int NL = sb_acc_blocks_in_lds(D, CB);
-    static_assert(NL == 0 || CB == 1, "LDS-resident ACC blocks for one column block per wave");
-    f32x4 *const accl = reinterpret_cast<f32x4 *>(lds + 2 * HALF + 2 * G::NKB * 4) + (threadIdx.x >> 6) * NL * 64;
 
     const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
     const int per = (n + 7) / 8;
@@ -1323,9 +1301,6 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
         state_init<D>(st[cb]);
         active |= (cg * NCOL + (wave * CB + cb) * 16) < ncols;
     }
-#pragma unroll
-    for (int k = 0; k < NL; ++k)
-        accl[k * 64 + (threadIdx.x & 63)] = f32x4{0.f, 0.f, 0.f, 0.f};
     int min_lim = 0x7fffffff;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
@@ -1379,22 +1354,10 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
         if (t < last)
             issue(true, t + 1);
         if (active) {
-            bool up;
             if ((t + 1) * G::T > min_lim)
-                up = prefill_softmax_stats<D, CB, true>(sc, cols, t, a.scale_log2, st, pf, f);
+                prefill_softmax<D, CB, true>(sc, cols, t, a.scale_log2, st, pf, f);
             else
-                up = prefill_softmax_stats<D, CB, false>(sc, cols, t, a.scale_log2, st, pf, f);
-            if (up) {
-                rescale_states<D, CB, NL>(st, f);
-#pragma unroll
-                for (int k = 0; k < NL; ++k) {
-                    f32x4 x = accl[k * 64 + (threadIdx.x & 63)];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        x[i] = __fmul_rn(x[i], f[0].gs);
-                    accl[k * 64 + (threadIdx.x & 63)] = x;
-                }
-            }
+                prefill_softmax<D, CB, false>(sc, cols, t, a.scale_log2, st, pf, f);
         }
         // V(t) (issued before K(t+1)) has landed
         if (t < last)
@@ -1407,7 +1370,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             __syncthreads();
         }
         if (active)
-            prefill_pv_grp<D, CB, 2, NL>(vbuf, pf, f, st, accl);
+            prefill_pv_grp<D, CB, 2>(vbuf, pf, f, st);      // two dim blocks at a time: registers are scarce
         __syncthreads();                                   // V(t) read by every wave
         if (t < last) {
             if (t + 2 <= last)
@@ -1418,9 +1381,6 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             __syncthreads();
         }
     }
-#pragma unroll
-    for (int k = 0; k < NL; ++k)
-        st[0].acc[G::NDB - NL + k] = accl[k * 64 + (threadIdx.x & 63)];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const ColInfo cj = col_info(a, cg * NCOL + (wave * CB + cb) * 16 + c, kvh, q0, q_len, seq_len);
@@ -2130,7 +2090,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
                 f[0].gs = x.gs[lane];
                 f[0].h = x.h[lane];
                 // ACC * gs inside the fold, for every tile (ACC * 1 is exact)
-                prefill_pv_grp<D, 1, (D == 128 ? 8 : 4), 0, true>(stage(t - 1) + HALF, pf, f, st);
+                prefill_pv_grp<D, 1, (D == 128 ? 8 : 4), true>(stage(t - 1) + HALF, pf, f, st);
             }
             __syncthreads();                               // done with the hand-off of t - 1
             if (t <= last) {
@@ -2340,7 +2300,7 @@ template <int D, int CB, int NWV, int WPE>
 static hipError_t prefill_sb_launch(AttnArgs a, hipStream_t s, uint64_t *blocks, int max_query_len)
 {
     constexpr int NCOL = NWV * CB * 16;
-    constexpr int LDS_BYTES = Geo<D>::LDS + 2 * Geo<D>::NKB * 4 + sb_acc_blocks_in_lds(D, CB) * 1024 * NWV;
+    constexpr int LDS_BYTES = Geo<D>::LDS + 2 * Geo<D>::NKB * 4;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     a.col_groups = (max_query_len * a.group + NCOL - 1) / NCOL;
     const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * a.col_groups;

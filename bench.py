@@ -339,7 +339,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the pool lives on one device); "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the pool lives on one device); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

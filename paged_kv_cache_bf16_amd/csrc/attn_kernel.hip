@@ -985,8 +985,10 @@ constexpr int kFoldUnits = kFoldTiles * (kFoldSlice / 4) / NT;   // 16-byte load
 
 // One round of the fold's inputs: the (acc, m, l) partials of tiles
 // t0 .. t0+nt-1 for one column and one 32-dim slice.  fold_load issues the
-// loads (rounds of whole workgroups past the last tile issue none);
-// fold_store waits for them and writes them to LDS.
+// (m, l) loads first, then the acc loads (rounds of whole workgroups past
+// the last tile issue none); fold_store_ml waits for the former only, so the
+// max scan runs while the acc partials are still in flight, and fold_store
+// waits for those and writes them to LDS.
 struct FoldRound {
     f32x4 v[kFoldUnits];
     float m, l;
@@ -997,6 +999,13 @@ __device__ __forceinline__ void fold_load(const AttnArgs &a, int64_t slot0, int 
                                           FoldRound &fr)
 {
     const int th = threadIdx.x;
+    fr.m = 0.f;
+    fr.l = 0.f;
+    if (th < kFoldTiles) {
+        const int64_t si = (slot0 + t0 + min(th, nt - 1)) * kSplitCols + col;
+        fr.m = a.ws_m[si];
+        fr.l = a.ws_l[si];
+    }
 #pragma unroll
     for (int r = 0; r < kFoldUnits; ++r) {
         if (r * NT >= nt * (kFoldSlice / 4))
@@ -1007,17 +1016,9 @@ __device__ __forceinline__ void fold_load(const AttnArgs &a, int64_t slot0, int 
         const int64_t si = (slot0 + t0 + tt) * kSplitCols + col;
         fr.v[r] = *reinterpret_cast<const f32x4 *>(a.ws_acc + si * D + d0 + 4 * q);
     }
-    fr.m = 0.f;
-    fr.l = 0.f;
-    if (th < kFoldTiles) {
-        const int64_t si = (slot0 + t0 + min(th, nt - 1)) * kSplitCols + col;
-        fr.m = a.ws_m[si];
-        fr.l = a.ws_l[si];
-    }
 }
 
-__device__ __forceinline__ void fold_store(const FoldRound &fr, int nt, float (*stage)[kFoldSlice], float *sm,
-                                           float *sl)
+__device__ __forceinline__ void fold_store(const FoldRound &fr, int nt, float (*stage)[kFoldSlice])
 {
     const int th = threadIdx.x;
 #pragma unroll
@@ -1029,6 +1030,11 @@ __device__ __forceinline__ void fold_store(const FoldRound &fr, int nt, float (*
         if (tt < nt)
             *reinterpret_cast<f32x4 *>(&stage[tt][4 * (u % (kFoldSlice / 4))]) = fr.v[r];
     }
+}
+
+__device__ __forceinline__ void fold_store_ml(const FoldRound &fr, int nt, float *sm, float *sl)
+{
+    const int th = threadIdx.x;
     if (th < nt) {
         sm[th] = fr.m;
         sl[th] = fr.l;
@@ -1065,7 +1071,6 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
     const int ncols = q_len * a.group;
     if (ncols > kSplitCols || col >= ncols)
         return;
-    fold_store(fr, nt0, stage, sm, sl);
     const int n_tiles = (seq_len + G::T - 1) / G::T;
 
     float M = -INFINITY, L = 0.f, acc = 0.f;
@@ -1074,8 +1079,8 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
         if (t0 > 0) {
             fold_load<D>(a, slot0, col, d0, t0, nt, fr);
             __syncthreads();
-            fold_store(fr, nt, stage, sm, sl);
         }
+        fold_store_ml(fr, nt, sm, sl);      // waits for the (m, l) loads only
         __syncthreads();
         // running max before each tile: inclusive wave scans, then wave totals
         float v = th < nt ? sm[th] : -INFINITY;
@@ -1099,6 +1104,7 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
             const FoldF f = fold_factors(ref_of(excl), sm[th]);
             sgh[th] = make_float2(f.gs, f.h);
         }
+        fold_store(fr, nt, stage);          // the partials, needed only by the chains
         __syncthreads();
         // wave 0 folds ACC (one dim per lane), wave 1 folds L, side by side;
         // every thread carries M (the next round's scan starts from it)

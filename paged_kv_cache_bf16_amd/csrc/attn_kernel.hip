@@ -986,9 +986,9 @@ constexpr int kFoldUnits = kFoldTiles * (kFoldSlice / 4) / NT;   // 16-byte load
 // One round of the fold's inputs: the (acc, m, l) partials of tiles
 // t0 .. t0+nt-1 for one column and one 32-dim slice.  fold_load issues the
 // (m, l) loads first, then the acc loads (rounds of whole workgroups past
-// the last tile issue none); fold_store_ml waits for the former only, so the
-// max scan runs while the acc partials are still in flight, and fold_store
-// waits for those and writes them to LDS.
+// the last tile issue none); the max scan reads the m values from the
+// registers of the threads that loaded them while the acc partials are still
+// in flight, and fold_store waits for those and writes them to LDS.
 struct FoldRound {
     f32x4 v[kFoldUnits];
     float m, l;
@@ -1032,14 +1032,6 @@ __device__ __forceinline__ void fold_store(const FoldRound &fr, int nt, float (*
     }
 }
 
-__device__ __forceinline__ void fold_store_ml(const FoldRound &fr, int nt, float *sm, float *sl)
-{
-    const int th = threadIdx.x;
-    if (th < nt) {
-        sm[th] = fr.m;
-        sl[th] = fr.l;
-    }
-}
 
 template <int D>
 __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
@@ -1047,7 +1039,7 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
     using G = Geo<D>;
     constexpr int NSL = D / kFoldSlice;
     __shared__ float stage[kFoldTiles][kFoldSlice];
-    __shared__ float sm[kFoldTiles], sl[kFoldTiles];
+    __shared__ float sl[kFoldTiles];
     __shared__ float2 sgh[kFoldTiles];         // (gs, h) of each tile: one LDS read per tile in the chains
     __shared__ float wmax[NW], sL;
 
@@ -1080,10 +1072,11 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
             fold_load<D>(a, slot0, col, d0, t0, nt, fr);
             __syncthreads();
         }
-        fold_store_ml(fr, nt, sm, sl);      // waits for the (m, l) loads only
-        __syncthreads();
-        // running max before each tile: inclusive wave scans, then wave totals
-        float v = th < nt ? sm[th] : -INFINITY;
+        // running max before each tile: inclusive wave scans, then wave
+        // totals; thread t holds tile t's max in a register (this waits for
+        // the (m, l) loads only)
+        const float mt = th < nt ? fr.m : -INFINITY;
+        float v = mt;
 #pragma unroll
         for (int off = 1; off < 64; off *= 2) {
             const float o = __shfl_up(v, off, 64);
@@ -1101,8 +1094,9 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
         float excl = __shfl_up(incl, 1, 64);
         excl = lane == 0 ? pre : excl;
         if (th < nt) {
-            const FoldF f = fold_factors(ref_of(excl), sm[th]);
+            const FoldF f = fold_factors(ref_of(excl), mt);
             sgh[th] = make_float2(f.gs, f.h);
+            sl[th] = fr.l;
         }
         fold_store(fr, nt, stage);          // the partials, needed only by the chains
         __syncthreads();

@@ -1001,8 +1001,8 @@ __device__ __forceinline__ void fold_load(const AttnArgs &a, int64_t slot0, int 
     const int th = threadIdx.x;
     fr.m = 0.f;
     fr.l = 0.f;
-    if (th < kFoldTiles) {
-        const int64_t si = (slot0 + t0 + min(th, nt - 1)) * kSplitCols + col;
+    if (th < nt) {                           // nt <= kFoldTiles: one tile per thread
+        const int64_t si = (slot0 + t0 + th) * kSplitCols + col;
         fr.m = a.ws_m[si];
         fr.l = a.ws_l[si];
     }

@@ -819,17 +819,24 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     }
 
     // ---- new tokens of this launch whose slots fall in this tile (FUSE):
-    // their keys come from the new rows, not from the pool (reloaded only in
-    // the waves that hold such a key)
+    // their keys and values come from the new rows, not from the pool.  A
+    // lane's K fragment is one token, so at most one new token replaces it;
+    // a lane's V fragment holds 8 consecutive tokens of one dim, any number
+    // of which may be new (consecutive positions of one sequence), so each of
+    // the 8 elements records its own token (8-bit field: index + 1, 0 =
+    // none).  The pool load of a fragment may race with this launch's scatter
+    // of the new tokens, but only in elements that are replaced here; the
+    // other elements are never written by the launch.
     if (FUSE) {
-        int knew[KPW], vnew[G::NKS], vel[G::NKS];
+        int knew[KPW];
+        uint64_t vidx[G::NKS];
 #pragma unroll
         for (int kl = 0; kl < KPW; ++kl)
             knew[kl] = -1;
 #pragma unroll
         for (int st = 0; st < G::NKS; ++st)
-            vnew[st] = -1, vel[st] = 0;
-        for (int jn = a.num_new - 1; jn >= 0; --jn) {       // the first matching token wins
+            vidx[st] = 0;
+        for (int jn = a.num_new - 1; jn >= 0; --jn) {       // for a shared slot, the first token wins
             const int64_t sj = ((int64_t)__builtin_amdgcn_readlane((int)(my_new >> 32), jn) << 32) |
                                (uint32_t)__builtin_amdgcn_readlane((int)my_new, jn);
             if (sj < 0 || sj >= a.num_blocks * BS)
@@ -844,12 +851,12 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
                 const int64_t bk = (c >> 3) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
                 knew[kl] = (bk == bj && tok == tj) ? jn : knew[kl];
             }
+            const int sh = 8 * (tj & 7);
 #pragma unroll
             for (int st = 0; st < G::NKS; ++st) {
                 const int64_t bv = (g >> 1) ? (int64_t)blk[2 * st + 1] : (int64_t)blk[2 * st];
                 const bool hit = bv == bj && (tj >> 3) == (g & 1);
-                vnew[st] = hit ? jn : vnew[st];
-                vel[st] = hit ? (tj & 7) : vel[st];
+                vidx[st] = hit ? (vidx[st] & ~(0xFFull << sh)) | ((uint64_t)(jn + 1) << sh) : vidx[st];
             }
         }
 #pragma unroll
@@ -861,17 +868,29 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
                     kf[kl][ds] = *reinterpret_cast<const bf16x8 *>(row + ds * 32);
             }
         }
+        bool vhit = false;
 #pragma unroll
-        for (int st = 0; st < G::NKS; ++st) {
-            if (vnew[st] >= 0) {
-                const int word = vel[st] >> 1, sh = (vel[st] & 1) * 16;
+        for (int st = 0; st < G::NKS; ++st)
+            vhit |= vidx[st] != 0;
+        if (__builtin_amdgcn_ballot_w64(vhit) != 0) {      // wave-uniform: only waves holding a new value
+            const uint16_t *vrow = a.new_v + (int64_t)kvh * D + 16 * (w * DPW) + c;
+            // one round per (step, element) that some lane of the wave replaces
+            // (a decode step with one new token per sequence: one round)
 #pragma unroll
-                for (int dl = 0; dl < DPW; ++dl) {
-                    const uint16_t x = a.new_v[vnew[st] * a.new_v_stride + (int64_t)kvh * D + 16 * (w * DPW + dl) + c];
+            for (int st = 0; st < G::NKS; ++st) {
 #pragma unroll
-                    for (int wd = 0; wd < 4; ++wd)
-                        if (wd == word)
-                            vraw[dl][st][wd] = (vraw[dl][st][wd] & ~(0xFFFFu << sh)) | ((uint32_t)x << sh);
+                for (int e = 0; e < 8; ++e) {
+                    const int id = (int)((vidx[st] >> (8 * e)) & 0xFF);
+                    if (__builtin_amdgcn_ballot_w64(id != 0) == 0)
+                        continue;
+                    if (id != 0) {
+                        const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+#pragma unroll
+                        for (int dl = 0; dl < DPW; ++dl) {
+                            const uint32_t x = vrow[(int64_t)(id - 1) * a.new_v_stride + 16 * dl];
+                            vraw[dl][st][e >> 1] = (vraw[dl][st][e >> 1] & keep) | (x << (16 * (e & 1)));
+                        }
+                    }
                 }
             }
         }

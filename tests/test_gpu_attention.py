@@ -9,10 +9,11 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_kv_cache_bf16_amd as kvp
 from paged_kv_cache_bf16_amd import workloads as wl
-from harness import (GpuCase, bitwise, bf16_to_f32, compare, dev_bits, host_bits, oracle_attention,
-                     oracle_pool, sample_rows)
+from harness import (GpuCase, bitwise, bf16_to_f32, compare, dev_bits, group_rows, host_bits,
+                     oracle_attention, oracle_pool, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -65,14 +66,22 @@ def test_decode_b4_kv7168():
     assert kvp.kvp_get_counters()["split_kv_launches"] >= 1
 
 
+def _rows(*parts):
+    return np.array(sorted(set(np.concatenate(parts).tolist())), np.int64)
+
+
 def test_prefill_b1_q4096_sampled():
+    """Every row of the first, a middle and the last 256-column workgroup
+    (64 query rows each at G = 4), plus a seeded sample."""
     w = wl.prefill()
-    _run_and_compare(w, rows=sample_rows(w, 160))
+    _run_and_compare(w, rows=_rows(group_rows(w, 64), sample_rows(w, 64)))
 
 
 def test_suffix_b4_q128_kv7168_sampled():
+    """Every row of the first, a middle and the last 64-column workgroup of
+    each sequence (16 query rows each), plus a seeded sample."""
     w = wl.suffix()
-    _run_and_compare(w, rows=sample_rows(w, 160))
+    _run_and_compare(w, rows=_rows(group_rows(w, 16), sample_rows(w, 64)))
 
 
 def test_ragged_mixed_batch_over_2gb_pool():
@@ -83,7 +92,8 @@ def test_ragged_mixed_batch_over_2gb_pool():
 @pytest.mark.parametrize("L", wl.WIDE_LENGTHS)
 def test_wide_head_prefill_sampled_and_decode(L):
     w = wl.wide(L)
-    g, out, _ = _run_and_compare(w, rows=sample_rows(w, 24), what="wide%d" % L)
+    # every row of the first, a middle and the last 128-column workgroup (16 rows at G = 8)
+    g, out, _ = _run_and_compare(w, rows=_rows(group_rows(w, 16), sample_rows(w, 24)), what="wide%d" % L)
     d = w.decode_view()
     g.set_queries(d.q, d.query_lens)
     dec = g.run()
@@ -194,15 +204,16 @@ def _run_step(w, slots, kn, vn, fused):
     k, v = dev_bits(kn), dev_bits(vn)
     sd = torch.from_numpy(slots).cuda()
     ms = int(w.seq_lens.max())
+    mq = int(w.max_query_len)
     g.out.fill_(-1)
     torch.cuda.synchronize()
     before = kvp.kvp_get_counters()
     if fused:
-        kvp.kvp_decode_step(g.pool, k, v, sd, g.q, g.out, w.num_q_heads, g.bt, g.seq_lens, g.qsl, 1, ms, w.scale,
+        kvp.kvp_decode_step(g.pool, k, v, sd, g.q, g.out, w.num_q_heads, g.bt, g.seq_lens, g.qsl, mq, ms, w.scale,
                             True, workspace=g.ws)
     else:
         kvp.reshape_and_cache(g.pool, k, v, sd)
-        kvp.paged_attention(g.pool, g.q, g.out, w.num_q_heads, g.bt, g.seq_lens, g.qsl, 1, ms, w.scale, True,
+        kvp.paged_attention(g.pool, g.q, g.out, w.num_q_heads, g.bt, g.seq_lens, g.qsl, mq, ms, w.scale, True,
                             workspace=g.ws)
     torch.cuda.synchronize()
     after = kvp.kvp_get_counters()
@@ -225,6 +236,52 @@ def test_decode_step_fused_equals_cache_then_attention(D, Hq, Hkv):
     bitwise(pool_f, pool_s, "pool after the fused step")
     bitwise(out_f, out_s, "output of the fused step")
     assert np.isfinite(bf16_to_f32(out_f)).all()
+
+
+def _multi_token_step_case(seed, lens, n_new, Hq, Hkv, D):
+    """A decode step that writes the last n_new positions of every row and
+    queries exactly those positions (q_len = n_new, bottom-right causal)."""
+    w = wl.random_case(seed, lens, [n_new] * len(lens), Hq, Hkv, D)
+    rng = np.random.default_rng(seed + 11)
+    slots = [int(w.block_tables[b, p // 16]) * 16 + p % 16 for b, L in enumerate(lens) for p in range(L - n_new, L)]
+    T = len(slots)
+    kn = wl.to_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    vn = wl.to_bf16_bits(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    return w, np.array(slots, np.int64), kn, vn
+
+
+# rows whose last positions cross a half-page (7/8), a page (15/16), a
+# 128-key tile (127/128), a 64-key tile (63/64), or stay inside one
+# half-page (696..699: several new values in one lane's 8-token V unit)
+MULTI_LENS = [9, 17, 130, 66, 700]
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,n_new,lens", [
+    (128, 8, 2, 2, MULTI_LENS), (128, 8, 2, 3, MULTI_LENS), (128, 8, 2, 4, MULTI_LENS),
+    (256, 8, 2, 2, MULTI_LENS), (256, 8, 2, 3, MULTI_LENS), (256, 8, 2, 4, MULTI_LENS),
+    (512, 8, 2, 2, MULTI_LENS), (512, 8, 2, 3, MULTI_LENS), (512, 8, 2, 4, MULTI_LENS),
+    (512, 16, 2, 2, MULTI_LENS),
+    (128, 2, 2, 16, [16, 40, 130, 700]), (256, 2, 2, 16, [16, 40, 130, 700]),
+    (512, 2, 2, 16, [16, 40, 130, 700]),
+], ids=lambda x: str(x) if not isinstance(x, list) else "L%d" % len(x))
+def test_decode_step_several_new_tokens_per_row(D, Hq, Hkv, n_new, lens):
+    """kvp_decode_step writing n_new consecutive tokens per row (all in one
+    launch): pool and output bits equal reshape_and_cache followed by
+    paged_attention, and the output matches the oracle run on the pool after
+    the scatter ("test(rocm): ReshapeAndCache->PagedAttention composition at
+    real dims", What changed: the cache write and the read that must see it)."""
+    print("multi-token step D=%d Hq=%d Hkv=%d n=%d lens=%s" % (D, Hq, Hkv, n_new, lens), flush=True)
+    w, slots, kn, vn = _multi_token_step_case(7 * D + 3 * n_new + Hq, lens, n_new, Hq, Hkv, D)
+    out_f, pool_f, delta = _run_step(w, slots, kn, vn, fused=True)
+    assert delta == {"fused_decode_steps": 1, "reshape_and_cache_launches": 0}
+    out_s, pool_s, delta_s = _run_step(w, slots, kn, vn, fused=False)
+    assert delta_s["reshape_and_cache_launches"] == 1
+    bitwise(pool_f, pool_s, "pool after the fused step")
+    bitwise(out_f, out_s, "output of the fused step")
+    opool = oracle_pool(w)
+    oracle.reshape_and_cache(opool, kn, vn, slots)
+    np.testing.assert_array_equal(pool_f, opool.storage)
+    compare(out_f, oracle_attention(w, opool), "multi-token step vs oracle")
 
 
 def test_decode_step_many_tokens_falls_back_to_two_launches():
@@ -254,6 +311,42 @@ def test_decode_long_rows():
     g.set_queries(w.q, w.query_lens)
     full = g.run()
     bitwise(dec, full[w.query_start_loc[1:] - 1], "long decode vs prefill last rows")
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,L,peak,vs", [
+    (128, 8, 2, 26000, 24999, 1.0),      # 128-key tiles: the peak in tile 195, past the first round of 192
+    (512, 16, 2, 18432, 15007, 0.5),     # 64-key tiles: tile 234 of 288 (the wide-head geometry)
+    (512, 16, 2, 13000, 12300, 0.5),     # tile 192: the first tile of the second fold round
+])
+def test_planted_peak_long_rows(D, Hq, Hkv, L, peak, vs):
+    """A long row whose running maximum jumps late: the key at position
+    `peak` is planted as alpha * q (q = the last query row's first head of
+    each kv-head group), so that head's softmax is nearly one-hot on it and
+    its output is ~V[peak] (magnitude ~1) while every other key's weight is
+    ~1e-5.  Decode (split-KV, partials folded in rounds of 192 tiles) and
+    the full prefill's last row must both find the peak: a fold that drops
+    or misweights the second round, or a reference that does not move,
+    returns ~mean(V) ~ 0 instead."""
+    print("planted peak D=%d L=%d peak=%d" % (D, L, peak), flush=True)
+    w = wl.random_case(500 + D + L, [L], [L], Hq, Hkv, D, value_scale=vs)
+    G = Hq // Hkv
+    alpha = 2.0 / vs                           # score ~ 22.6 natural-log units at either scale
+    qlast = bf16_to_f32(w.q[L - 1])            # [Hq, D]
+    k = w.k.copy()
+    for g in range(Hkv):
+        k[peak, g] = wl.to_bf16_bits(np.float32(alpha) * qlast[g * G])
+    w.k = k
+    g, full, dec = _prefill_then_decode(w)
+    d = w.decode_view()
+    ref = oracle_attention(d, oracle_pool(w))
+    # the pin is live: the oracle's planted heads return V[peak]
+    vpk = bf16_to_f32(w.v[peak])
+    for gg in range(Hkv):
+        assert np.abs(ref[0, gg * G] - vpk[gg]).max() < 1e-2
+    compare(dec, ref, "planted peak decode L=%d" % L)
+    bitwise(dec[0], full[L - 1], "planted peak decode vs prefill last row")
+    rows = _rows(group_rows(w, 16, groups=("last",)), sample_rows(w, 8))
+    compare(full[rows], oracle_attention(w, oracle_pool(w), rows=rows), "planted peak prefill L=%d" % L)
 
 
 # ------------------------------------------------------------ bitwise properties
@@ -327,15 +420,13 @@ def test_decode_with_larger_host_bound_is_bitwise_equal():
     compare(base, oracle_attention(w, oracle_pool(w)), "decode")
 
 
-def test_repeated_calls_are_deterministic_and_workspace_self_cleans():
+def test_repeated_calls_are_deterministic():
     w = wl.random_case(12, [3000, 40], [1, 1], 8, 2, 128)
     g = GpuCase(w)
     a = g.run()
     for _ in range(20):
         b = g.run()
     bitwise(a, b, "repeat")
-    ws_tickets = g.ws  # the tickets live at the end; a clean workspace repeats identically
-    assert ws_tickets.numel() > 0
 
 
 def test_empty_batch_and_zero_queries_are_noops():
@@ -394,9 +485,14 @@ def test_fused_qkv_view_strides():
     torch.cuda.synchronize()
     g = GpuCase(w)
     ref = g.run()
-    bitwise(host_bits(outv.contiguous()), ref, "fused-view prefill")
+    got = host_bits(outv.contiguous())
+    bitwise(got, ref, "fused-view prefill")
     assert (host_bits(wide[:, Hq * D:]) == 0xFFFF).all(), "wrote past the output rows"
     np.testing.assert_array_equal(host_bits(pool.storage), g.pool_bits())
+    # and against the oracle: the pool bit for bit, the output within tolerance
+    opool = oracle_pool(w)
+    np.testing.assert_array_equal(host_bits(pool.storage), opool.storage)
+    compare(got, oracle_attention(w, opool), "fused-view prefill vs oracle")
 
 
 def test_fused_qkv_view_decode_step():
@@ -424,6 +520,11 @@ def test_fused_qkv_view_decode_step():
     torch.cuda.synchronize()
     bitwise(host_bits(out), out_c, "fused-view decode step output")
     np.testing.assert_array_equal(g.pool_bits(), pool_c)
+    # and against the oracle run on the pool after the step's scatter
+    opool = oracle_pool(w)
+    oracle.reshape_and_cache(opool, kn, vn, slots)
+    np.testing.assert_array_equal(g.pool_bits(), opool.storage)
+    compare(host_bits(out), oracle_attention(w, opool), "fused-view decode step vs oracle")
 
 
 @pytest.mark.parametrize("lens,Hq,Hkv,D,ncol", [

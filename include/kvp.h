@@ -23,7 +23,9 @@
  *     is never retried and no other path is tried instead.
  *   - Device buffers (pool, q, k, v, out, tables, workspace) are owned by the
  *     caller.  The library owns only the small host-side pool descriptor and
- *     never allocates device memory.
+ *     never allocates device memory; its one device-resident object is the
+ *     fixed scratch array of paged_attention_noalloc, part of its code
+ *     object (KVP_SCRATCH_BYTES per device, held until the process ends).
  *   - Work is queued on the caller's stream (a hipStream_t passed as void*;
  *     NULL is the default stream).  No entry point synchronises the host.
  *   - Every launching entry point may be captured into a HIP graph: none
@@ -277,6 +279,38 @@ int kvp_decode_step(const kvp_pool *pool, const void *k, const void *v, int64_t 
                     int32_t block_table_stride, const int32_t *seq_lens, const int32_t *query_start_loc,
                     int32_t max_query_len, int32_t max_seq_len, float scale, int causal,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention_noalloc -- paged_attention for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments (minus the workspace), checks, kernels and bits as
+ * paged_attention; the split-KV partials go to a library-owned scratch
+ * array of KVP_SCRATCH_BYTES in device memory (a static __device__ array:
+ * each GPU the library runs on holds its own copy from module load until
+ * the process ends).  Nothing is allocated or freed by the call.
+ *   - A call that needs the split-KV path alone (max_query_len * G <= 16,
+ *     decode) and whose partials exceed KVP_SCRATCH_BYTES is rejected with
+ *     KVP_ERR_WORKSPACE_TOO_SMALL before anything is queued; the bytes a call
+ *     needs are kvp_workspace_bytes(pool, num_q_heads, num_seqs,
+ *     max_seq_len).  Other calls whose partials would not fit run every row
+ *     through the prefill kernels (same bits).
+ *   - Every call on one GPU uses that GPU's one array.  The array keeps the
+ *     last call's contents; every call writes the partials it reads before
+ *     reading them, so nothing needs clearing.  Two calls that can overlap
+ *     on one GPU (different streams, or different host threads) race on
+ *     the array: serialise them.
+ * Errors: those of paged_attention; KVP_ERR_HIP if the scratch address
+ * cannot be obtained (nothing queued).
+ */
+#define KVP_SCRATCH_BYTES (32u << 20)
+
+int paged_attention_noalloc(const kvp_pool *pool, const void *q, int64_t q_token_stride, void *out,
+                            int64_t out_token_stride, int32_t num_q_heads, int32_t num_seqs,
+                            const int32_t *block_tables, int32_t block_table_stride,
+                            const int32_t *seq_lens, const int32_t *query_start_loc,
+                            int32_t max_query_len, int32_t max_seq_len, float scale, int causal,
+                            void *stream);
 
 /* Dispatch counters: evidence of which kernel actually ran. */
 typedef struct {

@@ -72,6 +72,8 @@ def load_library(path: str = LIB_PATH):
                              ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I, P, SZ, P], I),
         "paged_attention_lse": ([P, P, I64, P, I64, P, I64, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32,
                                  P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I, P, SZ, P], I),
+        "paged_attention_noalloc": ([P, P, I64, P, I64, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I, P], I),
         "kvp_merge_attention": ([P, P, P, P, P, P, I64, ctypes.c_int32, ctypes.c_int32, P], I),
         "kvp_decode_step": ([P, P, P, I64, I64, I64, P, P, I64, P, I64, ctypes.c_int32, ctypes.c_int32, P,
                              ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I, P, SZ, P], I),
@@ -243,6 +245,23 @@ def paged_attention(pool: KVPool, q, out, num_q_heads: int, block_tables, seq_le
         _ptr(block_tables), int(block_tables.stride(0)), _ptr(seq_lens), _ptr(query_start_loc),
         int(max_query_len), int(max_seq_len), float(scale), int(bool(causal)), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+KVP_SCRATCH_BYTES = 32 << 20
+
+
+def paged_attention_noalloc(pool: KVPool, q, out, num_q_heads: int, block_tables, seq_lens, query_start_loc,
+                            max_query_len: int, max_seq_len: int, scale: float | None = None, causal: bool = True,
+                            stream=None) -> None:
+    """paged_attention with the split-KV partials in the library's own scratch
+    array (KVP_SCRATCH_BYTES per device; no workspace, nothing allocated)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(pool.head_dim)
+    B = int(seq_lens.shape[0])
+    _check(load_library().paged_attention_noalloc(
+        pool.handle, _ptr(q), int(q.stride(0)), _ptr(out), int(out.stride(0)), int(num_q_heads), B,
+        _ptr(block_tables), int(block_tables.stride(0)), _ptr(seq_lens), _ptr(query_start_loc),
+        int(max_query_len), int(max_seq_len), float(scale), int(bool(causal)), _stream(stream)))
 
 
 def paged_attention_lse(pool: KVPool, q, out, lse, num_q_heads: int, block_tables, seq_lens, query_start_loc,

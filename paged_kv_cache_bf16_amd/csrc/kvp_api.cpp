@@ -11,10 +11,16 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <unordered_map>
 
 #include "kvp_internal.h"
+
+// Scratch of paged_attention_noalloc: the split-KV partials of calls that
+// bring no workspace.  One copy per device (loaded with the code object);
+// host code never names it except to look up that device's address.
+static __device__ __align__(256) char scratch[KVP_SCRATCH_BYTES];
 
 namespace {
 
@@ -236,6 +242,34 @@ int launch_attention(kvp::AttnArgs a, const AttnPlan &plan, void *stream)
     return ok();
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (each device holds its own copy).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "paged_attention_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KVP_ERR_UNSUPPORTED, "paged_attention_noalloc: device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_fail(e, "paged_attention_noalloc: hipGetSymbolAddress(scratch)");
+        if (!p)
+            return fail(KVP_ERR_HIP, "paged_attention_noalloc: null scratch address");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return KVP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -418,6 +452,34 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
     const int rc = prepare_attention(pool, q, q_token_stride, out, out_token_stride, num_q_heads, num_seqs,
                                      block_tables, block_table_stride, seq_lens, query_start_loc, max_query_len,
                                      max_seq_len, scale, causal, workspace, workspace_bytes, a, plan);
+    if (rc != KVP_OK)
+        return rc;
+    if (plan.noop)
+        return ok();
+    return launch_attention(a, plan, stream);
+}
+
+int paged_attention_noalloc(const kvp_pool *pool, const void *q, int64_t q_token_stride, void *out,
+                            int64_t out_token_stride, int32_t num_q_heads, int32_t num_seqs,
+                            const int32_t *block_tables, int32_t block_table_stride, const int32_t *seq_lens,
+                            const int32_t *query_start_loc, int32_t max_query_len, int32_t max_seq_len, float scale,
+                            int causal, void *stream)
+{
+    void *ws = nullptr;
+    int rc = scratch_address(&ws);
+    if (rc != KVP_OK)
+        return rc;
+    kvp::AttnArgs a;
+    AttnPlan plan;
+    rc = prepare_attention(pool, q, q_token_stride, out, out_token_stride, num_q_heads, num_seqs, block_tables,
+                           block_table_stride, seq_lens, query_start_loc, max_query_len, max_seq_len, scale, causal,
+                           ws, KVP_SCRATCH_BYTES, a, plan);
+    if (rc == KVP_ERR_WORKSPACE_TOO_SMALL) {
+        char why[sizeof g_err];
+        snprintf(why, sizeof why, "%s", g_err);
+        return fail(rc, "paged_attention_noalloc: the split-KV partials of this call exceed the %u-byte scratch (%s)",
+                    (unsigned)KVP_SCRATCH_BYTES, why);
+    }
     if (rc != KVP_OK)
         return rc;
     if (plan.noop)

@@ -21,8 +21,8 @@
  * Numerics: the attention is the textbook definition evaluated on the
  * logically reassembled sequence, accumulated in FP32 (d ascending for the
  * dot products, keys ascending for the sums), with expf.  Parallelism is
- * only across independent output rows, so results do not depend on the
- * number of threads.
+ * only across independent (query row, head) outputs, so results do not
+ * depend on the number of threads.
  *
  * Pool layout (a format both sides must agree on; restated, not shared):
  *   block b, kv head h, token t (0..15), dim d:
@@ -127,49 +127,47 @@ static float v_logical(const uint16_t *v_pool, int64_t v_block_stride, const int
 }
 
 /*
- * One query row of paged attention, all heads.  b is the sequence, r the
- * query index within that sequence's queries.  Writes out[Hq][D] (FP32).
- * Returns the number of keys the row attended to.
+ * One query row of paged attention, one query head h.  b is the sequence, r
+ * the query index within that sequence's queries.  Writes out[h][D] (FP32)
+ * and lse[h].  Returns the number of keys the row attended to.
  */
 static int64_t attend_row(float *out, const uint16_t *qrow, const uint16_t *k_pool,
                           const uint16_t *v_pool, int64_t k_block_stride, int64_t v_block_stride,
                           const int32_t *bt_row, int64_t seq_len, int64_t q_len, int64_t r,
                           int Hq, int Hkv, int D, float scale, int causal,
-                          float *lse /* [Hq] or NULL */, float *s /* scratch [seq_len] */)
+                          float *lse /* [Hq] or NULL */, float *s /* scratch [seq_len] */, int h)
 {
     int G = Hq / Hkv;
     int64_t pos = seq_len - q_len + r;               /* bottom-right alignment */
     int64_t nkeys = causal ? pos + 1 : seq_len;      /* keys 0 .. nkeys-1 visible */
-    for (int h = 0; h < Hq; ++h) {
-        int g = h / G;
-        const uint16_t *qh = qrow + (int64_t)h * D;
-        /* scores: s_j = scale * sum_d q[d] * K_j[d], FP32, d ascending */
-        float m = -INFINITY;
-        for (int64_t j = 0; j < nkeys; ++j) {
-            float dot = 0.0f;
-            for (int d = 0; d < D; ++d)
-                dot += bf16_to_f32(qh[d]) * k_logical(k_pool, k_block_stride, bt_row, g, j, d, D);
-            s[j] = scale * dot;
-            if (s[j] > m)
-                m = s[j];
-        }
-        /* softmax weights and their sum, keys ascending */
-        float l = 0.0f;
-        for (int64_t j = 0; j < nkeys; ++j) {
-            s[j] = expf(s[j] - m);
-            l += s[j];
-        }
-        /* weighted sum of V rows, keys ascending, then normalise */
-        for (int d = 0; d < D; ++d) {
-            float acc = 0.0f;
-            for (int64_t j = 0; j < nkeys; ++j)
-                acc += s[j] * v_logical(v_pool, v_block_stride, bt_row, g, j, d, D);
-            out[(int64_t)h * D + d] = acc / l;
-        }
-        /* log-sum-exp of the scaled scores: log(sum_j exp(s_j)) = m + log(l) */
-        if (lse)
-            lse[h] = m + logf(l);
+    int g = h / G;
+    const uint16_t *qh = qrow + (int64_t)h * D;
+    /* scores: s_j = scale * sum_d q[d] * K_j[d], FP32, d ascending */
+    float m = -INFINITY;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        float dot = 0.0f;
+        for (int d = 0; d < D; ++d)
+            dot += bf16_to_f32(qh[d]) * k_logical(k_pool, k_block_stride, bt_row, g, j, d, D);
+        s[j] = scale * dot;
+        if (s[j] > m)
+            m = s[j];
     }
+    /* softmax weights and their sum, keys ascending */
+    float l = 0.0f;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        s[j] = expf(s[j] - m);
+        l += s[j];
+    }
+    /* weighted sum of V rows, keys ascending, then normalise */
+    for (int d = 0; d < D; ++d) {
+        float acc = 0.0f;
+        for (int64_t j = 0; j < nkeys; ++j)
+            acc += s[j] * v_logical(v_pool, v_block_stride, bt_row, g, j, d, D);
+        out[(int64_t)h * D + d] = acc / l;
+    }
+    /* log-sum-exp of the scaled scores: log(sum_j exp(s_j)) = m + log(l) */
+    if (lse)
+        lse[h] = m + logf(l);
     return nkeys;
 }
 
@@ -222,9 +220,11 @@ int oracle_paged_attention(float *out, const uint16_t *q, const uint16_t *k_pool
             failed = 1;
         }
 #pragma omp for schedule(dynamic, 1)
-        for (int64_t i = 0; i < count; ++i) {
+        for (int64_t ih = 0; ih < count * Hq; ++ih) {
             if (!s)
                 continue;
+            int64_t i = ih / Hq;
+            int h = (int)(ih % Hq);
             int64_t row = rows ? rows[i] : i;
             int b = 0;
             while (!(row >= query_start_loc[b] && row < query_start_loc[b + 1]))
@@ -233,7 +233,7 @@ int oracle_paged_attention(float *out, const uint16_t *q, const uint16_t *k_pool
             attend_row(out + i * (int64_t)Hq * D, q + row * (int64_t)Hq * D, k_pool, v_pool,
                        k_block_stride, v_block_stride, block_tables + (int64_t)b * W,
                        seq_lens[b], q_len, row - query_start_loc[b], Hq, Hkv, D, scale,
-                       causal, lse ? lse + i * (int64_t)Hq : NULL, s);
+                       causal, lse ? lse + i * (int64_t)Hq : NULL, s, h);
         }
         free(s);
     }

@@ -89,17 +89,32 @@ typedef struct {
 
 typedef struct kvp_pool kvp_pool;   /* opaque host-side descriptor */
 
-/* Validate desc and create a descriptor.  *out receives the handle.
+/* kv_pool_create -- validate desc and create a host-side descriptor over
+ * the caller's pool memory ("fix(rocm): stabilize direct paged CK attention
+ * for bitwise R/R", Changes: the attention consumes the serving engine's KV
+ * cache directly, and 64-bit addressing is kept when a K/V view spans more
+ * than 2 GB; Operator benchmarks: separate and interleaved pools, small and
+ * over 2 GB).  Validation happens here once, before any work is submitted
+ * ("ROCm: harden compact peer-local KV prefill for Gemma-4", Required
+ * hardening: invalid metadata and byte budgets are covered before
+ * submission).  *out receives the handle; the library reads `desc` only
+ * during this call.
  * Errors: INVALID_ARGUMENT (null, non-positive sizes, short strides,
  * misaligned pointers, overlapping K/V pages), UNSUPPORTED (head_dim,
  * block_size). */
 int kv_pool_create(const kvp_pool_desc *desc, kvp_pool **out);
 
-/* Release a descriptor (the caller's device memory is untouched). */
+/* Release a descriptor (the caller's device memory is untouched): the
+ * teardown half of the descriptor lifecycle ("ROCm: harden compact
+ * peer-local KV prefill for Gemma-4", Required hardening: persistent
+ * resource lifecycle, no progressive host-RAM growth). */
 int kv_pool_destroy(kvp_pool *pool);
 
-/* Total bytes spanned by the pool from its lowest to highest page byte
- * (what decides whether 32-bit offsets would overflow). */
+/* Total bytes spanned by the pool from its lowest to highest page byte:
+ * what decides whether 32-bit offsets would overflow ("fix(rocm): stabilize
+ * direct paged CK attention for bitwise R/R", Changes: 64-bit addressing
+ * when a K/V view spans more than 2 GB; every kernel here always forms block
+ * addresses in 64 bits, so this is informational). */
 int kv_pool_span_bytes(const kvp_pool *pool, int64_t *bytes);
 
 /*
@@ -123,7 +138,10 @@ int reshape_and_cache(const kvp_pool *pool, const void *k, const void *v, int64_
 
 /*
  * kvp_check_slot_mapping -- host-side check of a slot mapping (a debug aid
- * for the preconditions reshape_and_cache does not check on the device):
+ * for the preconditions reshape_and_cache does not check on the device;
+ * "test(rocm): ReshapeAndCache->PagedAttention composition at real dims",
+ * review thread: the slot of token i is block_table[i / 16] * 16 + i % 16,
+ * so a valid mapping names each slot at most once):
  * every slot is < num_blocks * 16 and no two tokens share a slot; negative
  * slots are allowed (skipped by the scatter).
  *   slots  host, [num_tokens] int64.
@@ -151,12 +169,22 @@ int kvp_check_slot_mapping(const kvp_pool *pool, const int64_t *slots, int64_t n
 int kv_prepare_block_tables(const kvp_pool *pool, const int32_t *block_tables, int32_t num_seqs,
                             int32_t width, const int32_t *seq_lens, int32_t *out);
 
-/* Width a prepared table has: width rounded up to a multiple of 8 pages. */
+/* Width a prepared table has: width rounded up to a multiple of 8 pages,
+ * i.e. whole 128-token KV tiles ("fix(rocm): stabilize direct paged CK
+ * attention for bitwise R/R", Changes: pad page tables to complete KV
+ * tiles). */
 int32_t kvp_padded_width(int32_t width);
 
 /*
  * Bytes of device workspace paged_attention needs for these bounds: the
  * per-tile partial softmax states (m, l, acc) of the split-KV (decode) path.
+ * No passage of the pages defines this call: the split-KV decode (one
+ * workgroup per KV tile, then a fold of the tile states in tile order) is
+ * this library's design for spreading a decode row over the chip under the
+ * fixed schedule of "fix(rocm): stabilize direct paged CK attention for
+ * bitwise R/R" (Changes).  The caller owns the buffer, so the library itself
+ * allocates nothing ("ROCm: harden compact peer-local KV prefill for
+ * Gemma-4", Required hardening: no progressive VRAM growth).
  * Every call writes the partials it reads before reading them, so the
  * workspace needs no initialisation and one workspace sized for the largest
  * bounds serves calls of any smaller batch or length.  One workspace must
@@ -166,7 +194,9 @@ int kvp_workspace_bytes(const kvp_pool *pool, int32_t num_q_heads, int32_t num_s
                         int32_t max_seq_len, size_t *bytes);
 
 /* Zero-fill a workspace on `stream` with a fill kernel (optional; useful to
- * make a fresh buffer's contents defined). */
+ * make a fresh buffer's contents defined).  No passage of the pages defines
+ * it; it is a fill kernel rather than a memset so that it may be captured
+ * into a HIP graph. */
 int kvp_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -312,7 +342,12 @@ int paged_attention_noalloc(const kvp_pool *pool, const void *q, int64_t q_token
                             int32_t max_query_len, int32_t max_seq_len, float scale, int causal,
                             void *stream);
 
-/* Dispatch counters: evidence of which kernel actually ran. */
+/* Dispatch counters: evidence of which kernel actually ran ("ROCm: harden
+ * compact peer-local KV prefill for Gemma-4", Required hardening: positive
+ * execution breadcrumb/counters, a dispatch miss invalidates a measurement;
+ * "fix(rocm): stabilize direct paged CK attention for bitwise R/R",
+ * Changes: report the entrypoint actually selected).  Process-wide,
+ * updated atomically by every launching call after a successful launch. */
 typedef struct {
     uint64_t reshape_and_cache_launches;
     uint64_t split_kv_launches;        /* decode / short-query kernel */
@@ -324,12 +359,18 @@ typedef struct {
 } kvp_counters;
 
 int kvp_get_counters(kvp_counters *out);
+/* Zero the dispatch counters (same passages as kvp_get_counters). */
 int kvp_reset_counters(void);
 
-/* Thread-local description of the last error ("" after success). */
+/* Thread-local description of the last error ("" after success), so that a
+ * failure before submission is reported with its reason and leaves nothing
+ * behind, and a failure after submission is reported, not retried ("ROCm:
+ * harden compact peer-local KV prefill for Gemma-4", Required hardening:
+ * pre-submit failures leave state unchanged; after any submission a failure
+ * is fatal, never double-submitted). */
 const char *kvp_last_error(void);
 
-/* Library version string. */
+/* Library version string (no passage of the pages; identifies the build). */
 const char *kvp_version(void);
 
 #ifdef __cplusplus

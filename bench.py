@@ -155,7 +155,7 @@ class Uploaded:
     """A workloads.Workload resident on the GPU: pool written through
     reshape_and_cache, prepared tables, queries, output and workspace."""
 
-    def __init__(self, w):
+    def __init__(self, w, split_cols=16):
         import torch
         import paged_kv_cache_bf16_amd as kvp
         self.kvp, self.w = kvp, w
@@ -172,7 +172,8 @@ class Uploaded:
         # a workspace only when some row is short (q_len * G <= 16), as a caller would pass it
         G = w.num_q_heads // w.num_kv_heads
         short = bool((w.query_lens * G <= 16).any())
-        self.ws = kvp.alloc_workspace(self.pool, w.num_q_heads, w.batch, self.max_s) if short else None
+        self.ws = (kvp.alloc_workspace(self.pool, w.num_q_heads, w.batch, self.max_s, split_cols=split_cols)
+                   if short or split_cols > 16 else None)
         torch.cuda.synchronize()
 
     def attention(self, _i=0):
@@ -365,9 +366,9 @@ def decode_sets(set_bytes, target=640 << 20, lo=8, hi=40):
     return int(min(hi, max(lo, -(-target // set_bytes))))
 
 
-def bench_prefill_config(name, w, stream, n_calls, with_cache=False):
+def bench_prefill_config(name, w, stream, n_calls, with_cache=False, split_cols=16):
     """A prefill-shaped workload from workloads.py: one paged_attention call per graph entry."""
-    up = Uploaded(w)
+    up = Uploaded(w, split_cols)
     G = w.num_q_heads // w.num_kv_heads
     flops = prefill_flops(w.head_dim, w.num_q_heads, w.seq_lens, w.query_lens, w.causal)
     nbytes = attention_bytes(w.head_dim, w.num_q_heads, w.num_kv_heads, w.seq_lens, w.query_lens)
@@ -376,7 +377,7 @@ def bench_prefill_config(name, w, stream, n_calls, with_cache=False):
     c0 = up.kvp.kvp_get_counters()
     r["kernel_grid_blocks"] = c0["last_grid_blocks"]
     r["groups_us"] = [round(t, 3) for t in ts]
-    r["workspace"] = up.ws is not None
+    r["workspace"] = None if up.ws is None else "kvp_workspace_bytes_split(..., %d)" % split_cols
     if with_cache:
         cus, _ = graph_us(up.cache_write, max(1, n_calls), stream)
         cb = 2 * 2 * int(w.slot_mapping.shape[0]) * w.num_kv_heads * w.head_dim * 2 + 8 * int(w.slot_mapping.shape[0])
@@ -423,9 +424,11 @@ def run_config(name, stream):
         return {"workload": "suffix prefill B4 Q128 on KV7168 Hq32 Hkv8 Dh128, reversed pages",
                 "prefill": bench_prefill_config("suffix B4 Q128", wl.suffix(), stream, 20)}
     if name == "ragged":
+        w = wl.ragged()
         return {"workload": "ragged B4 KV {513,4096,4171,7168}, query tails {full,128,17,1}, Hq8 Hkv2 Dh128, "
                             "2.29 GB interleaved pool (pages above 2^31 B), padded poisoned tables",
-                "prefill": bench_prefill_config("ragged", wl.ragged(), stream, 20)}
+                "prefill": bench_prefill_config("ragged", w, stream, 20),
+                "prefill_wide_split": bench_prefill_config("ragged, split_cols 512", w, stream, 20, split_cols=512)}
     if name.startswith("wide"):
         L = int(name[4:])
         w = wl.wide(L)

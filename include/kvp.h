@@ -193,6 +193,25 @@ int32_t kvp_padded_width(int32_t width);
 int kvp_workspace_bytes(const kvp_pool *pool, int32_t num_q_heads, int32_t num_seqs,
                         int32_t max_seq_len, size_t *bytes);
 
+/*
+ * Bytes of a workspace that also lets the rows of a mixed batch with up to
+ * split_cols columns (q_len * G <= split_cols; split_cols a multiple of 16
+ * in [16, 1024]) take the split-KV path: their KV tiles are spread over the
+ * chip (one workgroup per tile and group of four 16-column blocks) and their
+ * tile states folded in tile order, instead of streaming every tile through
+ * one prefill workgroup.  Same bits either way (the fixed schedule of
+ * "fix(rocm): stabilize direct paged CK attention for bitwise R/R",
+ * Changes); faster when the batch's long-query rows leave the GPU idle and
+ * its medium rows have long KV (the ragged batches of that page's
+ * Additional checks: tails of 128 and 17 queries on 4096/4171 keys).  The
+ * partials take split_cols * (head_dim + 2) * 4 bytes per (row, kv head,
+ * KV tile).  paged_attention picks the widest limit (a multiple of 16, at
+ * most max_query_len * G rounded up, at most 1024) whose partials fit the
+ * workspace it is given.
+ */
+int kvp_workspace_bytes_split(const kvp_pool *pool, int32_t num_q_heads, int32_t num_seqs,
+                              int32_t max_seq_len, int32_t split_cols, size_t *bytes);
+
 /* Zero-fill a workspace on `stream` with a fill kernel (optional; useful to
  * make a fresh buffer's contents defined).  No passage of the pages defines
  * it; it is a fill kernel rather than a memset so that it may be captured
@@ -227,7 +246,10 @@ int kvp_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
  *                    max_query_len * G <= 16 (decode).  Otherwise optional:
  *                    given (large enough) with num_seqs > 1, rows whose
  *                    q_len * G <= 16 take the split-KV decode path and the
- *                    others the prefill path, in two launches on `stream`.
+ *                    others the prefill path, in two launches on `stream`;
+ *                    a workspace of kvp_workspace_bytes_split(..., S) bytes
+ *                    moves the rows with q_len * G <= S to the split-KV
+ *                    path as well.
  *                    The host cannot see the query lengths, so a batch
  *                    given a workspace launches the split-KV kernels even
  *                    when none of its rows is short (they then only read

@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH):
         "kvp_padded_width": ([ctypes.c_int32], ctypes.c_int32),
         "kvp_check_slot_mapping": ([P, P, I64], I),
         "kvp_workspace_bytes": ([P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(SZ)], I),
+        "kvp_workspace_bytes_split": ([P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.POINTER(SZ)], I),
         "kvp_workspace_init": ([P, SZ, P], I),
         "paged_attention": ([P, P, I64, P, I64, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P, P,
                              ctypes.c_int32, ctypes.c_int32, ctypes.c_float, I, P, SZ, P], I),
@@ -216,14 +218,24 @@ def kvp_workspace_bytes(pool: KVPool, num_q_heads: int, num_seqs: int, max_seq_l
     return out.value
 
 
+def kvp_workspace_bytes_split(pool: KVPool, num_q_heads: int, num_seqs: int, max_seq_len: int,
+                              split_cols: int) -> int:
+    out = ctypes.c_size_t()
+    _check(load_library().kvp_workspace_bytes_split(pool.handle, int(num_q_heads), int(num_seqs), int(max_seq_len),
+                                                    int(split_cols), ctypes.byref(out)))
+    return out.value
+
+
 def kvp_workspace_init(workspace, stream=None) -> None:
     _check(load_library().kvp_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
                                              _stream(stream)))
 
 
-def alloc_workspace(pool: KVPool, num_q_heads: int, num_seqs: int, max_seq_len: int, device="cuda"):
+def alloc_workspace(pool: KVPool, num_q_heads: int, num_seqs: int, max_seq_len: int, device="cuda",
+                    split_cols: int = 16):
     import torch
-    n = kvp_workspace_bytes(pool, num_q_heads, num_seqs, max_seq_len)
+    n = (kvp_workspace_bytes(pool, num_q_heads, num_seqs, max_seq_len) if split_cols == 16 else
+         kvp_workspace_bytes_split(pool, num_q_heads, num_seqs, max_seq_len, split_cols))
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
     kvp_workspace_init(ws)
     return ws

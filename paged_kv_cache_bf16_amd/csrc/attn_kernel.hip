@@ -720,7 +720,7 @@ __device__ __forceinline__ void scatter_new_tokens(const AttnArgs &a, int kvh)
     }
 }
 
-template <int D, bool FUSE>
+template <int D, bool FUSE, bool MULTI>
 __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
 {
     using G = Geo<D>;
@@ -737,11 +737,12 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     __shared__ bf16x8 sq[QL ? G::NDS : 1][64];
 
     const int tile = blockIdx.x;
-    const int kvh = blockIdx.y;
+    const int kvh = blockIdx.y % a.num_kv_heads;
+    const int cbg = MULTI ? (int)blockIdx.y / a.num_kv_heads : 0;   // column-block group (MULTI: split_cols > 16)
     const int b = blockIdx.z;
     if (FUSE && tile == a.max_tiles) {
         // the extra column of workgroups writes the new tokens (kv head kvh)
-        if (b == 0)
+        if (b == 0 && cbg == 0)
             scatter_new_tokens<D>(a, kvh);
         return;
     }
@@ -762,32 +763,41 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     if (!row_ok(a, b, q0, q_len, seq_len))
         return;
     const int ncols = q_len * a.group;
-    if (ncols > kSplitCols)
+    if (ncols > a.split_cols)
         return;
     const int n_tiles = (seq_len + G::T - 1) / G::T;
     if (tile >= n_tiles)
+        return;
+    // this workgroup's 16-column blocks of the row
+    const int cb0 = cbg * kSplitGroupBlocks;
+    const int cb1 = MULTI ? min(cb0 + kSplitGroupBlocks, (ncols + 15) / 16) : 1;
+    if (cb0 >= cb1)
         return;
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, c = lane & 15;
     const int64_t hoff = (int64_t)kvh * BS * D;
 
-
     // ---- issue every load of this workgroup up front (non-temporal: each
-    // K/V byte is read once per call, so the lines need not stay cached)
+    // K/V byte is read once per call, so the lines need not stay cached);
+    // the K/V fragments serve every column block of the workgroup, Q is
+    // loaded per column block (the next block's while the current one runs)
     Cols<D> cols;
-    const ColInfo ci = col_info(a, c, kvh, q0, q_len, seq_len);
     constexpr int QPW = G::NDS / NW;               // dim steps of Q each wave stages (QL)
     bf16x8 qpart[QL ? QPW : 1];
-    if (QL) {
-        const uint16_t *src = a.q + (ci.lim > 0 ? ci.row : ci.row0) * a.q_token_stride + (int64_t)ci.head * D + 8 * g;
+    auto fetch_q = [&](int cb) {
+        const ColInfo cq = col_info(a, cb * 16 + c, kvh, q0, q_len, seq_len);
+        if (QL) {
+            const uint16_t *src = a.q + (cq.lim > 0 ? cq.row : cq.row0) * a.q_token_stride + (int64_t)cq.head * D + 8 * g;
 #pragma unroll
-        for (int k = 0; k < QPW; ++k)
-            qpart[k] = *reinterpret_cast<const bf16x8 *>(src + 32 * (w * QPW + k));
-        cols.lim = ci.lim;
-    } else {
-        load_q<D>(cols, a, ci);
-    }
+            for (int k = 0; k < QPW; ++k)
+                qpart[k] = *reinterpret_cast<const bf16x8 *>(src + 32 * (w * QPW + k));
+            cols.lim = cq.lim;
+        } else {
+            load_q<D>(cols, a, cq);
+        }
+    };
+    fetch_q(cb0);
     bf16x8 kf[KPW][G::NDS];
 #pragma unroll
     for (int kl = 0; kl < KPW; ++kl) {
@@ -811,12 +821,6 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     }
     // keep every load above ahead of the first use of any of them
     __builtin_amdgcn_sched_barrier(0);
-    if (QL) {
-#pragma unroll
-        for (int k = 0; k < QPW; ++k)
-            sq[w * QPW + k][lane] = qpart[k];
-        __syncthreads();
-    }
 
     // ---- new tokens of this launch whose slots fall in this tile (FUSE):
     // their keys and values come from the new rows, not from the pool.  A
@@ -904,87 +908,102 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
             vf[dl][st] = __builtin_bit_cast(bf16x8, valid >= BS ? vraw[dl][st] : mask_tokens(vraw[dl][st], 8 * (g & 1), valid));
     }
 
-    // ---- S for this wave's key blocks; scale, mask, wave max
-    f32x4 s[KPW];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kl = 0; kl < KPW; ++kl) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < G::NDS; ++ds)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kl][ds], QL ? sq[ds][lane] : cols.qf[QL ? 0 : ds], acc,
-                                                          0, 0, 0);
-        const int kb = w * KPW + kl;
-        const int st = kb >> 1, e = kb & 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = tile * G::T + 32 * st + 8 * g + 4 * e + i;
-            s[kl][i] = key < cols.lim ? acc[i] : -INFINITY;
-        }
-        mx = fmax2(mx, fmax2(fmax2(s[kl][0], s[kl][1]), fmax2(s[kl][2], s[kl][3])));
-    }
-    mx = max_xor32(max_xor16(mx));
-    if (g == 0)
-        smax[w][c] = mx;
-    __syncthreads();
-    mx = __fmul_rn(fmax2(fmax2(smax[0][c], smax[1][c]), fmax2(smax[2][c], smax[3][c])), a.scale_log2);
-    const float nmu = mx == -INFINITY ? 0.f : -mx;
-
-    // ---- p, this wave's level of the sum tree, P^T values to LDS
-    float part[KPW];
-#pragma unroll
-    for (int kl = 0; kl < KPW; ++kl) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            s[kl][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kl][i], a.scale_log2, nmu));
-        part[kl] = __fadd_rn(__fadd_rn(s[kl][0], s[kl][1]), __fadd_rn(s[kl][2], s[kl][3]));
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const __bf16 lo = (__bf16)s[kl][2 * h], hi = (__bf16)s[kl][2 * h + 1];
-            spf[w][2 * kl + h][lane] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                                       ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
-    }
-    ssum[w][lane] = KPW == 2 ? __fadd_rn(part[0], part[KPW - 1]) : part[0];
-    __syncthreads();
-
-    // ---- l: remaining levels of the tree, then across lanes
-    float l = __fadd_rn(__fadd_rn(ssum[0][lane], ssum[1][lane]), __fadd_rn(ssum[2][lane], ssum[3][lane]));
-    l = sum_xor32(sum_xor16(l));
-
-    // ---- P^T operands of every 32-key step, then P.V for this wave's dims
-    bf16x8 pf[G::NKS];
-#pragma unroll
-    for (int st = 0; st < G::NKS; ++st) {
-        u32x4 u;
-        if (KPW == 2) {
-            u = u32x4{spf[st][0][lane], spf[st][1][lane], spf[st][2][lane], spf[st][3][lane]};
-        } else {
-            u = u32x4{spf[2 * st][0][lane], spf[2 * st][1][lane], spf[2 * st + 1][0][lane], spf[2 * st + 1][1][lane]};
-        }
-        pf[st] = __builtin_bit_cast(bf16x8, u);
-    }
     const int64_t slot = ((int64_t)b * a.num_kv_heads + kvh) * a.max_tiles + tile;
-    float *accp = a.ws_acc + (slot * kSplitCols + c) * D + 4 * g;
+    for (int cb = cb0; cb < cb1; ++cb) {
+        if (MULTI && cb > cb0)
+            __syncthreads();                          // the previous block's LDS exchanges are read
+        if (QL) {
 #pragma unroll
-    for (int dl = 0; dl < DPW; ++dl) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < G::NKS; ++st)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dl][st], pf[st], acc, 0, 0, 0);
-        if (c < ncols) {
-            // head_dim 512: 16 KB of partials per tile (an eighth of the tile's
-            // K/V bytes) stream out during the kernel instead of leaving the
-            // L2 dirty for its end
-            if (D == 512)
-                __builtin_nontemporal_store(acc, reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)));
-            else
-                *reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)) = acc;
+            for (int k = 0; k < QPW; ++k)
+                sq[w * QPW + k][lane] = qpart[k];
+            __syncthreads();
         }
-    }
-    if (w == 0 && g == 0 && c < ncols) {
-        a.ws_m[slot * kSplitCols + c] = mx;
-        a.ws_l[slot * kSplitCols + c] = l;
+        const int col = cb * 16 + c;
+
+        // ---- S for this wave's key blocks; scale, mask, wave max
+        f32x4 s[KPW];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kl = 0; kl < KPW; ++kl) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ds = 0; ds < G::NDS; ++ds)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kl][ds], QL ? sq[ds][lane] : cols.qf[QL ? 0 : ds],
+                                                              acc, 0, 0, 0);
+            const int kb = w * KPW + kl;
+            const int st = kb >> 1, e = kb & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = tile * G::T + 32 * st + 8 * g + 4 * e + i;
+                s[kl][i] = key < cols.lim ? acc[i] : -INFINITY;
+            }
+            mx = fmax2(mx, fmax2(fmax2(s[kl][0], s[kl][1]), fmax2(s[kl][2], s[kl][3])));
+        }
+        // the next column block's Q, in flight during this block's softmax and P.V
+        if (MULTI && cb + 1 < cb1)
+            fetch_q(cb + 1);
+        mx = max_xor32(max_xor16(mx));
+        if (g == 0)
+            smax[w][c] = mx;
+        __syncthreads();
+        mx = __fmul_rn(fmax2(fmax2(smax[0][c], smax[1][c]), fmax2(smax[2][c], smax[3][c])), a.scale_log2);
+        const float nmu = mx == -INFINITY ? 0.f : -mx;
+
+        // ---- p, this wave's level of the sum tree, P^T values to LDS
+        float part[KPW];
+#pragma unroll
+        for (int kl = 0; kl < KPW; ++kl) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s[kl][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kl][i], a.scale_log2, nmu));
+            part[kl] = __fadd_rn(__fadd_rn(s[kl][0], s[kl][1]), __fadd_rn(s[kl][2], s[kl][3]));
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const __bf16 lo = (__bf16)s[kl][2 * h], hi = (__bf16)s[kl][2 * h + 1];
+                spf[w][2 * kl + h][lane] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                                           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            }
+        }
+        ssum[w][lane] = KPW == 2 ? __fadd_rn(part[0], part[KPW - 1]) : part[0];
+        __syncthreads();
+
+        // ---- l: remaining levels of the tree, then across lanes
+        float l = __fadd_rn(__fadd_rn(ssum[0][lane], ssum[1][lane]), __fadd_rn(ssum[2][lane], ssum[3][lane]));
+        l = sum_xor32(sum_xor16(l));
+
+        // ---- P^T operands of every 32-key step, then P.V for this wave's dims
+        bf16x8 pf[G::NKS];
+#pragma unroll
+        for (int st = 0; st < G::NKS; ++st) {
+            u32x4 u;
+            if (KPW == 2) {
+                u = u32x4{spf[st][0][lane], spf[st][1][lane], spf[st][2][lane], spf[st][3][lane]};
+            } else {
+                u = u32x4{spf[2 * st][0][lane], spf[2 * st][1][lane], spf[2 * st + 1][0][lane], spf[2 * st + 1][1][lane]};
+            }
+            pf[st] = __builtin_bit_cast(bf16x8, u);
+        }
+        float *accp = a.ws_acc + (slot * a.split_cols + col) * D + 4 * g;
+#pragma unroll
+        for (int dl = 0; dl < DPW; ++dl) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < G::NKS; ++st)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dl][st], pf[st], acc, 0, 0, 0);
+            if (col < ncols) {
+                // head_dim 512: 16 KB of partials per tile (an eighth of the tile's
+                // K/V bytes) stream out during the kernel instead of leaving the
+                // L2 dirty for its end
+                if (D == 512)
+                    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)));
+                else
+                    *reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)) = acc;
+            }
+        }
+        if (w == 0 && g == 0 && col < ncols) {
+            a.ws_m[slot * a.split_cols + col] = mx;
+            a.ws_l[slot * a.split_cols + col] = l;
+        }
     }
 }
 
@@ -1021,7 +1040,7 @@ __device__ __forceinline__ void fold_load(const AttnArgs &a, int64_t slot0, int 
     fr.m = 0.f;
     fr.l = 0.f;
     if (th < nt) {                           // nt <= kFoldTiles: one tile per thread
-        const int64_t si = (slot0 + t0 + th) * kSplitCols + col;
+        const int64_t si = (slot0 + t0 + th) * a.split_cols + col;
         fr.m = a.ws_m[si];
         fr.l = a.ws_l[si];
     }
@@ -1032,7 +1051,7 @@ __device__ __forceinline__ void fold_load(const AttnArgs &a, int64_t slot0, int 
         const int u = th + r * NT;
         const int tt = min(u / (kFoldSlice / 4), nt - 1);
         const int q = u % (kFoldSlice / 4);
-        const int64_t si = (slot0 + t0 + tt) * kSplitCols + col;
+        const int64_t si = (slot0 + t0 + tt) * a.split_cols + col;
         fr.v[r] = *reinterpret_cast<const f32x4 *>(a.ws_acc + si * D + d0 + 4 * q);
     }
 }
@@ -1080,7 +1099,7 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
     if (!row_ok(a, b, q0, q_len, seq_len))
         return;
     const int ncols = q_len * a.group;
-    if (ncols > kSplitCols || col >= ncols)
+    if (ncols > a.split_cols || col >= ncols)
         return;
     const int n_tiles = (seq_len + G::T - 1) / G::T;
 
@@ -1144,6 +1163,118 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
         const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
         a.out[ci.row * a.out_token_stride + (int64_t)ci.head * D + d0 + th] = finish1(acc, 1.0f / L);
         if (a.lse && slice == 0 && th == 0)
+            a.lse[ci.row * a.lse_token_stride + ci.head] = lse_of(ref_of(M), L);
+    }
+}
+
+// Fold kernel for rows with many columns (split_cols > 16).  Workgroup =
+// (kFoldWideCols consecutive columns, 32-dim slice, kv head, sequence), one
+// wave per column: in rounds of up to 64 tiles, lane t of the wave loads the
+// column's (m, l) of tile t and the wave scans the running max (the same
+// prefix max and the same fold factors as split_fold_kernel); all waves stage
+// the round's acc partials of the workgroup's columns in LDS; then lanes 0-31
+// of each wave run the ACC chain of one dim and lane 32 the L chain, in tile
+// order.  Same operations per (column, dim), so the same bits.
+constexpr int kFoldWideCols = 8;
+constexpr int kFoldWideTiles = 64;
+
+template <int D>
+__global__ __launch_bounds__(64 * kFoldWideCols) void split_fold_wide_kernel(AttnArgs a)
+{
+    using G = Geo<D>;
+    constexpr int NSL = D / kFoldSlice;
+    constexpr int NTH = 64 * kFoldWideCols;
+    constexpr int UNITS = kFoldWideCols * kFoldWideTiles * (kFoldSlice / 4);     // 16-byte acc units per round
+    static_assert(UNITS % NTH == 0, "whole units per thread");
+    constexpr int UPT = UNITS / NTH;
+    __shared__ float stage[kFoldWideCols][kFoldWideTiles][kFoldSlice];
+    __shared__ float2 sgh[kFoldWideCols][kFoldWideTiles];
+    __shared__ float sl[kFoldWideCols][kFoldWideTiles];
+
+    const int slice = blockIdx.x % NSL;
+    const int col0 = (blockIdx.x / NSL) * kFoldWideCols;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int th = threadIdx.x, lane = th & 63, w = th >> 6;
+    int q0, q_len, seq_len;
+    if (!row_ok(a, b, q0, q_len, seq_len))
+        return;
+    const int ncols = q_len * a.group;
+    if (ncols > a.split_cols || col0 >= ncols)
+        return;
+    const int col = col0 + w;                      // this wave's column (may be past the row's last)
+    const int n_tiles = (seq_len + G::T - 1) / G::T;
+    const int64_t slot0 = ((int64_t)b * a.num_kv_heads + kvh) * a.max_tiles;
+    const int d0 = slice * kFoldSlice;
+
+    float M = -INFINITY, L = 0.f, acc = 0.f;
+    for (int t0 = 0; t0 < n_tiles; t0 += kFoldWideTiles) {
+        const int nt = min(kFoldWideTiles, n_tiles - t0);
+        if (t0 > 0)
+            __syncthreads();                       // the previous round's LDS is read
+        // (m, l) of tile t0 + lane of this wave's column, and the acc units of the round
+        float mt = -INFINITY, lt = 0.f;
+        if (lane < nt && col < ncols) {
+            const int64_t si = (slot0 + t0 + lane) * a.split_cols + col;
+            mt = a.ws_m[si];
+            lt = a.ws_l[si];
+        }
+        f32x4 v[UPT];
+#pragma unroll
+        for (int r = 0; r < UPT; ++r) {
+            const int u = th + r * NTH;
+            const int q = u % (kFoldSlice / 4);
+            const int tt = (u / (kFoldSlice / 4)) % kFoldWideTiles;
+            const int cc = u / (kFoldSlice / 4) / kFoldWideTiles;
+            v[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (tt < nt && col0 + cc < ncols)
+                v[r] = *reinterpret_cast<const f32x4 *>(a.ws_acc + ((slot0 + t0 + tt) * a.split_cols + col0 + cc) * D +
+                                                        d0 + 4 * q);
+        }
+        // running max before each tile (lane = tile), from the running max M of earlier rounds
+        float incl = mt;
+#pragma unroll
+        for (int off = 1; off < 64; off *= 2) {
+            const float o = __shfl_up(incl, off, 64);
+            incl = lane >= off ? fmax2(incl, o) : incl;
+        }
+        incl = fmax2(incl, M);
+        float excl = __shfl_up(incl, 1, 64);
+        excl = lane == 0 ? M : excl;
+        if (lane < nt) {
+            const FoldF f = fold_factors(ref_of(excl), mt);
+            sgh[w][lane] = make_float2(f.gs, f.h);
+            sl[w][lane] = lt;
+        }
+        M = __shfl(incl, 63, 64);
+#pragma unroll
+        for (int r = 0; r < UPT; ++r) {
+            const int u = th + r * NTH;
+            const int q = u % (kFoldSlice / 4);
+            const int tt = (u / (kFoldSlice / 4)) % kFoldWideTiles;
+            const int cc = u / (kFoldSlice / 4) / kFoldWideTiles;
+            *reinterpret_cast<f32x4 *>(&stage[cc][tt][4 * q]) = v[r];
+        }
+        __syncthreads();
+        if (lane < kFoldSlice) {
+#pragma unroll 8
+            for (int tt = 0; tt < nt; ++tt) {
+                const float2 gh = sgh[w][tt];
+                acc = fold1v(acc, stage[w][tt][lane], gh.x, gh.y);
+            }
+        } else if (lane == kFoldSlice) {
+#pragma unroll 8
+            for (int tt = 0; tt < nt; ++tt) {
+                const float2 gh = sgh[w][tt];
+                L = fold1v(L, sl[w][tt], gh.x, gh.y);
+            }
+        }
+    }
+    L = __shfl(L, kFoldSlice, 64);
+    if (col < ncols && lane < kFoldSlice) {
+        const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
+        a.out[ci.row * a.out_token_stride + (int64_t)ci.head * D + d0 + lane] = finish1(acc, 1.0f / L);
+        if (a.lse && slice == 0 && lane == 0)
             a.lse[ci.row * a.lse_token_stride + ci.head] = lse_of(ref_of(M), L);
     }
 }
@@ -2455,16 +2586,28 @@ static hipError_t split_launch(const AttnArgs &a, int max_query_len, hipStream_t
 {
     if (a.max_tiles <= 0 || a.num_seqs <= 0)
         return hipSuccess;
-    const dim3 grid((unsigned)a.max_tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    if (fuse)   // one more column of workgroups for the cache write
-        hipLaunchKernelGGL((split_partial_kernel<D, true>), dim3(grid.x + 1, grid.y, grid.z), dim3(NT), 0, s, a);
+    // columns a row of this call can have on the split path, in groups of
+    // kSplitGroupBlocks 16-column blocks per workgroup
+    const int max_cols = (int)min((int64_t)a.split_cols, (int64_t)max_query_len * a.group);
+    const int groups = ((max_cols + 15) / 16 + kSplitGroupBlocks - 1) / kSplitGroupBlocks;
+    const dim3 grid((unsigned)a.max_tiles, (unsigned)(a.num_kv_heads * groups), (unsigned)a.num_seqs);
+    if (fuse)   // one more column of workgroups for the cache write (decode: one column block)
+        hipLaunchKernelGGL((split_partial_kernel<D, true, false>), dim3(grid.x + 1, grid.y, grid.z), dim3(NT), 0, s, a);
+    else if (a.split_cols > kSplitCols)
+        hipLaunchKernelGGL((split_partial_kernel<D, false, true>), grid, dim3(NT), 0, s, a);
     else
-        hipLaunchKernelGGL((split_partial_kernel<D, false>), grid, dim3(NT), 0, s, a);
-    // one fold workgroup per (column that can exist, 32-dim slice)
-    const int max_cols = min(kSplitCols, max_query_len * a.group);
-    const dim3 fgrid((unsigned)(max_cols * (D / kFoldSlice)), (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    hipLaunchKernelGGL((split_fold_kernel<D>), fgrid, dim3(NT), 0, s, a);
-    *blocks = (uint64_t)a.max_tiles * a.num_kv_heads * a.num_seqs;
+        hipLaunchKernelGGL((split_partial_kernel<D, false, false>), grid, dim3(NT), 0, s, a);
+    if (a.split_cols > kSplitCols) {
+        // one fold workgroup per (kFoldWideCols columns, 32-dim slice)
+        const dim3 fgrid((unsigned)((max_cols + kFoldWideCols - 1) / kFoldWideCols * (D / kFoldSlice)),
+                         (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+        hipLaunchKernelGGL((split_fold_wide_kernel<D>), fgrid, dim3(64 * kFoldWideCols), 0, s, a);
+    } else {
+        // one fold workgroup per (column that can exist, 32-dim slice)
+        const dim3 fgrid((unsigned)(max_cols * (D / kFoldSlice)), (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+        hipLaunchKernelGGL((split_fold_kernel<D>), fgrid, dim3(NT), 0, s, a);
+    }
+    *blocks = (uint64_t)grid.x * grid.y * grid.z;
     return hipGetLastError();
 }
 
@@ -2480,7 +2623,7 @@ hipError_t launch_split_kv(const AttnArgs &a, int head_dim, int max_query_len, h
 
 hipError_t launch_split_kv_fused(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks)
 {
-    if (a.num_new > kMaxFusedTokens)
+    if (a.num_new > kMaxFusedTokens || a.split_cols != kSplitCols)
         return hipErrorInvalidValue;
     switch (head_dim) {
     case 128: return split_launch<128>(a, max_query_len, s, blocks, true);
@@ -2490,14 +2633,16 @@ hipError_t launch_split_kv_fused(const AttnArgs &a, int head_dim, int max_query_
     }
 }
 
-Workspace workspace_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t max_tiles, int64_t head_dim)
+Workspace workspace_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t max_tiles, int64_t head_dim,
+                           int64_t split_cols)
 {
-    // Per-tile partials of the split-KV path.  Every call rewrites the slots
-    // it reads before reading them, so the workspace needs no initialisation
-    // and one workspace sized for the largest bounds serves smaller calls.
+    // Per-tile partials of the split-KV path, split_cols columns per (row,
+    // kv head, tile).  Every call rewrites the slots it reads before reading
+    // them, so the workspace needs no initialisation and one workspace sized
+    // for the largest bounds serves smaller calls.
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     Workspace w;
-    const size_t slots = (size_t)num_seqs * num_kv_heads * max_tiles * kSplitCols;
+    const size_t slots = (size_t)num_seqs * num_kv_heads * max_tiles * split_cols;
     w.acc_off = 0;
     w.m_off = up(w.acc_off + slots * head_dim * sizeof(float));
     w.l_off = up(w.m_off + slots * sizeof(float));

@@ -6,6 +6,7 @@
 // prefill for Gemma-4" (Required hardening: failures before submission leave
 // state unchanged; after submission a failure is reported, never retried or
 // routed elsewhere).
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -189,11 +190,17 @@ int prepare_attention(const kvp_pool *pool, const void *q, int64_t q_token_strid
     // path, which spreads their KV tiles over the chip; the rest stream
     // through a prefill kernel.  A call with only such rows needs the
     // workspace; a mixed batch of several rows uses both paths when a large
-    // enough workspace is given (both paths give the same bits per row).
+    // enough workspace is given (both paths give the same bits per row).  A
+    // mixed batch whose workspace holds the partials of wider rows sends the
+    // rows with up to that many columns (a multiple of 16, at most
+    // kMaxSplitCols) to the split-KV path as well: the widest limit that fits.
     const bool split_only = (int64_t)max_query_len * G <= kvp::kSplitCols;
-    if (num_seqs > 65535 || d.num_kv_heads > 65535)
-        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_seqs and num_kv_heads must be <= 65535");
-    const kvp::Workspace w = kvp::workspace_layout(num_seqs, d.num_kv_heads, a.max_tiles, D);
+    // launch grids: rows in gridDim.z, kv heads x column-block groups in gridDim.y
+    constexpr int kMaxGroups = (kvp::kMaxSplitCols / 16 + kvp::kSplitGroupBlocks - 1) / kvp::kSplitGroupBlocks;
+    if (num_seqs > 65535 || (int64_t)d.num_kv_heads * kMaxGroups > 65535)
+        return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_seqs must be <= 65535 and num_kv_heads <= %d",
+                    65535 / kMaxGroups);
+    kvp::Workspace w = kvp::workspace_layout(num_seqs, d.num_kv_heads, a.max_tiles, D, kvp::kSplitCols);
     const bool ws_ok = workspace && aligned16(workspace) && workspace_bytes >= w.total;
     if (split_only) {
         if (!workspace || !aligned16(workspace))
@@ -203,11 +210,24 @@ int prepare_attention(const kvp_pool *pool, const void *q, int64_t q_token_strid
                         w.total);
     }
     const bool use_split = split_only || (num_seqs > 1 && ws_ok);
+    int split_cols = kvp::kSplitCols;
+    if (use_split && !split_only) {
+        const int64_t widest = std::min<int64_t>(((int64_t)max_query_len * G + 15) / 16 * 16, kvp::kMaxSplitCols);
+        for (int64_t sc = widest; sc > kvp::kSplitCols; sc -= 16) {
+            const kvp::Workspace wsc = kvp::workspace_layout(num_seqs, d.num_kv_heads, a.max_tiles, D, sc);
+            if (workspace_bytes >= wsc.total) {
+                split_cols = (int)sc;
+                w = wsc;
+                break;
+            }
+        }
+    }
     if (use_split) {
         char *base = (char *)workspace;
         a.ws_acc = (float *)(base + w.acc_off);
         a.ws_m = (float *)(base + w.m_off);
         a.ws_l = (float *)(base + w.l_off);
+        a.split_cols = split_cols;
     }
     plan.noop = false;
     plan.split = use_split;
@@ -229,7 +249,6 @@ int launch_attention(kvp::AttnArgs a, const AttnPlan &plan, void *stream)
         if (a.num_new > 0)
             g_fused_steps++;
         g_last_grid = blocks;
-        a.split_cols = kvp::kSplitCols;
     }
     if (plan.prefill) {
         uint64_t blocks = 0;
@@ -422,8 +441,25 @@ int kvp_workspace_bytes(const kvp_pool *pool, int32_t num_q_heads, int32_t num_s
     if (num_q_heads <= 0 || num_seqs < 0 || max_seq_len < 0)
         return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_workspace_bytes: bad sizes");
     const int T = kvp::tile_tokens(pool->d.head_dim);
-    const kvp::Workspace w =
-        kvp::workspace_layout(num_seqs, pool->d.num_kv_heads, cdiv(max_seq_len, T), pool->d.head_dim);
+    const kvp::Workspace w = kvp::workspace_layout(num_seqs, pool->d.num_kv_heads, cdiv(max_seq_len, T),
+                                                   pool->d.head_dim, kvp::kSplitCols);
+    *bytes = w.total;
+    return ok();
+}
+
+int kvp_workspace_bytes_split(const kvp_pool *pool, int32_t num_q_heads, int32_t num_seqs, int32_t max_seq_len,
+                              int32_t split_cols, size_t *bytes)
+{
+    if (!pool || !bytes)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_workspace_bytes_split: null argument");
+    if (num_q_heads <= 0 || num_seqs < 0 || max_seq_len < 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_workspace_bytes_split: bad sizes");
+    if (split_cols < kvp::kSplitCols || split_cols > kvp::kMaxSplitCols || split_cols % 16)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kvp_workspace_bytes_split: split_cols %d must be a multiple of 16 in "
+                                              "[%d, %d]", split_cols, kvp::kSplitCols, kvp::kMaxSplitCols);
+    const int T = kvp::tile_tokens(pool->d.head_dim);
+    const kvp::Workspace w = kvp::workspace_layout(num_seqs, pool->d.num_kv_heads, cdiv(max_seq_len, T),
+                                                   pool->d.head_dim, split_cols);
     *bytes = w.total;
     return ok();
 }

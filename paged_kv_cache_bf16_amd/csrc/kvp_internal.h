@@ -18,8 +18,14 @@ namespace kvp {
 // contract: tile boundaries sit at multiples of this many absolute positions.
 constexpr int tile_tokens(int head_dim) { return head_dim == 128 ? 128 : 64; }
 
-// Columns (query position x head-in-group pairs) one split-KV workgroup owns.
+// Columns (query position x head-in-group pairs) of one MFMA column block:
+// rows with at most this many columns always take the split-KV path.
 constexpr int kSplitCols = 16;
+// A larger workspace lets rows with up to kMaxSplitCols columns take the
+// split-KV path too (each partial workgroup then runs up to
+// kSplitGroupBlocks column blocks of its tile).
+constexpr int kMaxSplitCols = 1024;
+constexpr int kSplitGroupBlocks = 4;
 
 struct CacheArgs {
     const uint16_t *k, *v;
@@ -43,13 +49,14 @@ struct AttnArgs {
     int32_t max_seq_len, max_tiles, col_groups;
     float scale_log2;          // softmax scale * log2(e), rounded once on the host
     int32_t causal;
-    int32_t split_cols;        // prefill kernels skip rows with q_len * G <= split_cols
+    int32_t split_cols;        // rows with q_len * G <= split_cols take the split-KV path (prefill kernels
+                               // skip them); 0 when it does not run.  Also the workspace's columns per slot.
     // optional log-sum-exp output [total_q][num_q_heads] (token stride below)
     float *lse;
     int64_t lse_token_stride;
     // split-KV workspace
-    float *ws_acc;             // [B][Hkv][max_tiles][kSplitCols][D]
-    float *ws_m, *ws_l;        // [B][Hkv][max_tiles][kSplitCols]
+    float *ws_acc;             // [B][Hkv][max_tiles][split_cols][D]
+    float *ws_m, *ws_l;        // [B][Hkv][max_tiles][split_cols]
     // new tokens written into the pool by the same launch (decode step):
     // token i's K/V rows, its slot (< 0: none); keys in those slots are read
     // from these rows, not from the pool
@@ -66,7 +73,8 @@ struct Workspace {
     size_t acc_off, m_off, l_off, total;
 };
 
-Workspace workspace_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t max_tiles, int64_t head_dim);
+Workspace workspace_layout(int64_t num_seqs, int64_t num_kv_heads, int64_t max_tiles, int64_t head_dim,
+                           int64_t split_cols);
 
 hipError_t launch_reshape_and_cache(const CacheArgs &a, hipStream_t s, uint64_t *blocks);
 // Split-KV path: per-tile partial kernel, then the fold kernel.

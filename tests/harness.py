@@ -38,7 +38,7 @@ class GpuCase:
     """A workload resident on the GPU: pool filled through reshape_and_cache,
     prepared tables and metadata, and a workspace."""
 
-    def __init__(self, w: wl.Workload, fill_bits=POISON, ws_max_seq_len=None):
+    def __init__(self, w: wl.Workload, fill_bits=POISON, ws_max_seq_len=None, split_cols=16):
         self.w = w
         self.pool = kvp.alloc_pool(w.num_blocks, w.num_kv_heads, w.head_dim, interleaved=w.interleaved,
                                    fill_bits=fill_bits)
@@ -48,7 +48,7 @@ class GpuCase:
         kvp.reshape_and_cache(self.pool, self.k, self.v, self.slots)
         self.set_queries(w.q, w.query_lens)
         self.ws = kvp.alloc_workspace(self.pool, w.num_q_heads, w.batch,
-                                      int(ws_max_seq_len or w.seq_lens.max(initial=1)))
+                                      int(ws_max_seq_len or w.seq_lens.max(initial=1)), split_cols=split_cols)
 
     def set_queries(self, q_bits, query_lens, block_tables=None, seq_lens=None):
         w = self.w

@@ -238,6 +238,48 @@ def test_decode_step_fused_equals_cache_then_attention(D, Hq, Hkv):
     assert np.isfinite(bf16_to_f32(out_f)).all()
 
 
+@pytest.mark.parametrize("D,Hq,Hkv,split_cols", [(128, 8, 2, 512), (128, 32, 8, 128), (256, 8, 2, 256),
+                                                  (512, 16, 2, 384)])
+def test_wide_split_mixed_batch_equals_prefill(D, Hq, Hkv, split_cols):
+    """A workspace of kvp_workspace_bytes_split(..., split_cols) sends the
+    rows with q_len * G <= split_cols to the split-KV path (several 16-column
+    blocks per partial workgroup, in groups of four); the others stream
+    through a prefill kernel.  Every row's output and lse equal the
+    prefill-only call (no workspace) bitwise, and match the oracle."""
+    G = Hq // Hkv
+    lens = [2100, 900, 1500, 3000, 640, 2000]
+    qls = [1, 5, max(1, 68 // G), max(1, split_cols // G), 300, max(1, split_cols // G + 1)]
+    w = wl.random_case(800 + D + split_cols, lens, qls, Hq, Hkv, D)
+    print("wide split D=%d G=%d split_cols=%d cols=%s" % (D, G, split_cols, [q * G for q in qls]), flush=True)
+    g = GpuCase(w, split_cols=split_cols)
+    c0 = kvp.kvp_get_counters()
+    out, lse = g.run_lse()
+    c1 = kvp.kvp_get_counters()
+    assert c1["split_kv_launches"] == c0["split_kv_launches"] + 1
+    assert c1["prefill_launches"] == c0["prefill_launches"] + 1
+    ref_out, ref_lse = g.run_lse(use_workspace=False)
+    bitwise(out, ref_out, "wide split vs prefill only")
+    assert np.array_equal(lse.view(np.uint32), ref_lse.view(np.uint32)), "lse differs"
+    rows = _rows(sample_rows(w, 48), group_rows(w, 4, groups=("last",)))
+    compare(out[rows], oracle_attention(w, oracle_pool(w), rows=rows), "wide split vs oracle")
+
+
+def test_wide_split_ragged_over_2gb():
+    """The ragged batch on its 2.29 GB pool with a workspace wide enough for
+    its 128- and 17-query rows (512 columns): same bits as with the minimal
+    workspace (only the one-query row on the split path) and within tolerance
+    of the oracle."""
+    w = wl.ragged()
+    g = GpuCase(w)
+    base = g.run()
+    ws_small = g.ws
+    g.ws = kvp.alloc_workspace(g.pool, w.num_q_heads, w.batch, int(w.seq_lens.max()), split_cols=512)
+    assert g.ws.numel() > ws_small.numel()
+    wide = g.run()
+    bitwise(wide, base, "ragged: wide split vs minimal workspace")
+    compare(wide, oracle_attention(w, oracle_pool(w)), "ragged wide split vs oracle")
+
+
 def _multi_token_step_case(seed, lens, n_new, Hq, Hkv, D):
     """A decode step that writes the last n_new positions of every row and
     queries exactly those positions (q_len = n_new, bottom-right causal)."""

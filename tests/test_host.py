@@ -267,3 +267,16 @@ def test_check_slot_mapping_agrees_with_the_oracle(lib):
     assert seen[True] > 50 and seen[False] > 50
     kvp.kvp_check_slot_mapping(pool, np.array([], np.int64))
     del pool                                  # the wrapper destroys the descriptor
+
+
+def test_workspace_bytes_split_sizes_and_errors(lib):
+    h = create(lib)[1]
+    pool = kvp.KVPool(h, make_desc(), None)
+    base = kvp.kvp_workspace_bytes(pool, 8, 4, 7168)
+    assert kvp.kvp_workspace_bytes_split(pool, 8, 4, 7168, 16) == base
+    w512 = kvp.kvp_workspace_bytes_split(pool, 8, 4, 7168, 512)
+    # 4 rows x 2 kv heads x 56 tiles x 512 columns x (128 + 2) floats, in 256-byte aligned parts
+    assert w512 >= 4 * 2 * 56 * 512 * (128 + 2) * 4 and w512 < 4 * 2 * 56 * 512 * (128 + 2) * 4 + 3 * 256
+    for bad in (0, 8, 24, 1040):
+        with pytest.raises(kvp.KvpError):
+            kvp.kvp_workspace_bytes_split(pool, 8, 4, 7168, bad)

@@ -502,10 +502,13 @@ __device__ __forceinline__ void prefill_qk_wide(const char *kl, const Cols<D> (&
 // Phase 2: softmax statistics and BF16 P^T of the tile, the fold factors
 // and the (R, L) fold; returns whether some column's reference moved (its
 // ACC must then be rescaled by gs before this tile's P.V is added).
+// The tile's statistics: mx = the scaled max of the scores each column sees
+// (-inf if none), lsum = the sum tree of p = exp2(fma(S, scale_log2, -mx)),
+// and P^T in BF16 (the same values the split-KV partial kernel stores).
 template <int D, int CB, bool MASK>
-__device__ __forceinline__ bool prefill_softmax_stats(f32x4 (&s)[CB][Geo<D>::NKB], const Cols<D> (&cols)[CB],
-                                                      int tile, float scale_log2, State<D> (&st)[CB],
-                                                      bf16x8 (&pf)[CB][Geo<D>::NKS], FoldF (&f)[CB])
+__device__ __forceinline__ void tile_stats(f32x4 (&s)[CB][Geo<D>::NKB], const Cols<D> (&cols)[CB], int tile,
+                                           float scale_log2, float (&mx)[CB], float (&lsum)[CB],
+                                           bf16x8 (&pf)[CB][Geo<D>::NKS])
 {
     using G = Geo<D>;
     const int lane = threadIdx.x & 63;
@@ -514,7 +517,6 @@ __device__ __forceinline__ bool prefill_softmax_stats(f32x4 (&s)[CB][Geo<D>::NKB
     // The max runs over raw scores (scale_log2 > 0, so max(S) * scale_log2
     // is the max of the scaled scores); p = exp2(fma(S, scale_log2, -m)).
     const int key0 = tile * G::T;
-    float mx[CB], lsum[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         float vals[4 * G::NKB];
@@ -565,6 +567,15 @@ __device__ __forceinline__ bool prefill_softmax_stats(f32x4 (&s)[CB][Geo<D>::NKB
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
         lsum[cb] = sum_xor32(sum_xor16(lsum[cb]));
+}
+
+template <int D, int CB, bool MASK>
+__device__ __forceinline__ bool prefill_softmax_stats(f32x4 (&s)[CB][Geo<D>::NKB], const Cols<D> (&cols)[CB],
+                                                      int tile, float scale_log2, State<D> (&st)[CB],
+                                                      bf16x8 (&pf)[CB][Geo<D>::NKS], FoldF (&f)[CB])
+{
+    float mx[CB], lsum[CB];
+    tile_stats<D, CB, MASK>(s, cols, tile, scale_log2, mx, lsum, pf);
 
     // ---- fold factors; one wave-uniform choice of fold sequence per tile
     bool any_up = false;
@@ -720,7 +731,7 @@ __device__ __forceinline__ void scatter_new_tokens(const AttnArgs &a, int kvh)
     }
 }
 
-template <int D, bool FUSE, bool MULTI>
+template <int D, bool FUSE>
 __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
 {
     using G = Geo<D>;
@@ -737,12 +748,11 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     __shared__ bf16x8 sq[QL ? G::NDS : 1][64];
 
     const int tile = blockIdx.x;
-    const int kvh = blockIdx.y % a.num_kv_heads;
-    const int cbg = MULTI ? (int)blockIdx.y / a.num_kv_heads : 0;   // column-block group (MULTI: split_cols > 16)
+    const int kvh = blockIdx.y;
     const int b = blockIdx.z;
     if (FUSE && tile == a.max_tiles) {
         // the extra column of workgroups writes the new tokens (kv head kvh)
-        if (b == 0 && cbg == 0)
+        if (b == 0)
             scatter_new_tokens<D>(a, kvh);
         return;
     }
@@ -768,36 +778,27 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     const int n_tiles = (seq_len + G::T - 1) / G::T;
     if (tile >= n_tiles)
         return;
-    // this workgroup's 16-column blocks of the row
-    const int cb0 = cbg * kSplitGroupBlocks;
-    const int cb1 = MULTI ? min(cb0 + kSplitGroupBlocks, (ncols + 15) / 16) : 1;
-    if (cb0 >= cb1)
-        return;
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, c = lane & 15;
     const int64_t hoff = (int64_t)kvh * BS * D;
 
+
     // ---- issue every load of this workgroup up front (non-temporal: each
-    // K/V byte is read once per call, so the lines need not stay cached);
-    // the K/V fragments serve every column block of the workgroup, Q is
-    // loaded per column block (the next block's while the current one runs)
+    // K/V byte is read once per call, so the lines need not stay cached)
     Cols<D> cols;
+    const ColInfo ci = col_info(a, c, kvh, q0, q_len, seq_len);
     constexpr int QPW = G::NDS / NW;               // dim steps of Q each wave stages (QL)
     bf16x8 qpart[QL ? QPW : 1];
-    auto fetch_q = [&](int cb) {
-        const ColInfo cq = col_info(a, cb * 16 + c, kvh, q0, q_len, seq_len);
-        if (QL) {
-            const uint16_t *src = a.q + (cq.lim > 0 ? cq.row : cq.row0) * a.q_token_stride + (int64_t)cq.head * D + 8 * g;
+    if (QL) {
+        const uint16_t *src = a.q + (ci.lim > 0 ? ci.row : ci.row0) * a.q_token_stride + (int64_t)ci.head * D + 8 * g;
 #pragma unroll
-            for (int k = 0; k < QPW; ++k)
-                qpart[k] = *reinterpret_cast<const bf16x8 *>(src + 32 * (w * QPW + k));
-            cols.lim = cq.lim;
-        } else {
-            load_q<D>(cols, a, cq);
-        }
-    };
-    fetch_q(cb0);
+        for (int k = 0; k < QPW; ++k)
+            qpart[k] = *reinterpret_cast<const bf16x8 *>(src + 32 * (w * QPW + k));
+        cols.lim = ci.lim;
+    } else {
+        load_q<D>(cols, a, ci);
+    }
     bf16x8 kf[KPW][G::NDS];
 #pragma unroll
     for (int kl = 0; kl < KPW; ++kl) {
@@ -821,6 +822,12 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     }
     // keep every load above ahead of the first use of any of them
     __builtin_amdgcn_sched_barrier(0);
+    if (QL) {
+#pragma unroll
+        for (int k = 0; k < QPW; ++k)
+            sq[w * QPW + k][lane] = qpart[k];
+        __syncthreads();
+    }
 
     // ---- new tokens of this launch whose slots fall in this tile (FUSE):
     // their keys and values come from the new rows, not from the pool.  A
@@ -908,102 +915,87 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
             vf[dl][st] = __builtin_bit_cast(bf16x8, valid >= BS ? vraw[dl][st] : mask_tokens(vraw[dl][st], 8 * (g & 1), valid));
     }
 
+    // ---- S for this wave's key blocks; scale, mask, wave max
+    f32x4 s[KPW];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kl = 0; kl < KPW; ++kl) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < G::NDS; ++ds)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kl][ds], QL ? sq[ds][lane] : cols.qf[QL ? 0 : ds], acc,
+                                                          0, 0, 0);
+        const int kb = w * KPW + kl;
+        const int st = kb >> 1, e = kb & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = tile * G::T + 32 * st + 8 * g + 4 * e + i;
+            s[kl][i] = key < cols.lim ? acc[i] : -INFINITY;
+        }
+        mx = fmax2(mx, fmax2(fmax2(s[kl][0], s[kl][1]), fmax2(s[kl][2], s[kl][3])));
+    }
+    mx = max_xor32(max_xor16(mx));
+    if (g == 0)
+        smax[w][c] = mx;
+    __syncthreads();
+    mx = __fmul_rn(fmax2(fmax2(smax[0][c], smax[1][c]), fmax2(smax[2][c], smax[3][c])), a.scale_log2);
+    const float nmu = mx == -INFINITY ? 0.f : -mx;
+
+    // ---- p, this wave's level of the sum tree, P^T values to LDS
+    float part[KPW];
+#pragma unroll
+    for (int kl = 0; kl < KPW; ++kl) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s[kl][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kl][i], a.scale_log2, nmu));
+        part[kl] = __fadd_rn(__fadd_rn(s[kl][0], s[kl][1]), __fadd_rn(s[kl][2], s[kl][3]));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const __bf16 lo = (__bf16)s[kl][2 * h], hi = (__bf16)s[kl][2 * h + 1];
+            spf[w][2 * kl + h][lane] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                                       ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+    }
+    ssum[w][lane] = KPW == 2 ? __fadd_rn(part[0], part[KPW - 1]) : part[0];
+    __syncthreads();
+
+    // ---- l: remaining levels of the tree, then across lanes
+    float l = __fadd_rn(__fadd_rn(ssum[0][lane], ssum[1][lane]), __fadd_rn(ssum[2][lane], ssum[3][lane]));
+    l = sum_xor32(sum_xor16(l));
+
+    // ---- P^T operands of every 32-key step, then P.V for this wave's dims
+    bf16x8 pf[G::NKS];
+#pragma unroll
+    for (int st = 0; st < G::NKS; ++st) {
+        u32x4 u;
+        if (KPW == 2) {
+            u = u32x4{spf[st][0][lane], spf[st][1][lane], spf[st][2][lane], spf[st][3][lane]};
+        } else {
+            u = u32x4{spf[2 * st][0][lane], spf[2 * st][1][lane], spf[2 * st + 1][0][lane], spf[2 * st + 1][1][lane]};
+        }
+        pf[st] = __builtin_bit_cast(bf16x8, u);
+    }
     const int64_t slot = ((int64_t)b * a.num_kv_heads + kvh) * a.max_tiles + tile;
-    for (int cb = cb0; cb < cb1; ++cb) {
-        if (MULTI && cb > cb0)
-            __syncthreads();                          // the previous block's LDS exchanges are read
-        if (QL) {
+    float *accp = a.ws_acc + (slot * a.split_cols + c) * D + 4 * g;
 #pragma unroll
-            for (int k = 0; k < QPW; ++k)
-                sq[w * QPW + k][lane] = qpart[k];
-            __syncthreads();
+    for (int dl = 0; dl < DPW; ++dl) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < G::NKS; ++st)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dl][st], pf[st], acc, 0, 0, 0);
+        if (c < ncols) {
+            // head_dim 512: 16 KB of partials per tile (an eighth of the tile's
+            // K/V bytes) stream out during the kernel instead of leaving the
+            // L2 dirty for its end
+            if (D == 512)
+                __builtin_nontemporal_store(acc, reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)));
+            else
+                *reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)) = acc;
         }
-        const int col = cb * 16 + c;
-
-        // ---- S for this wave's key blocks; scale, mask, wave max
-        f32x4 s[KPW];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kl = 0; kl < KPW; ++kl) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ds = 0; ds < G::NDS; ++ds)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kl][ds], QL ? sq[ds][lane] : cols.qf[QL ? 0 : ds],
-                                                              acc, 0, 0, 0);
-            const int kb = w * KPW + kl;
-            const int st = kb >> 1, e = kb & 1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = tile * G::T + 32 * st + 8 * g + 4 * e + i;
-                s[kl][i] = key < cols.lim ? acc[i] : -INFINITY;
-            }
-            mx = fmax2(mx, fmax2(fmax2(s[kl][0], s[kl][1]), fmax2(s[kl][2], s[kl][3])));
-        }
-        // the next column block's Q, in flight during this block's softmax and P.V
-        if (MULTI && cb + 1 < cb1)
-            fetch_q(cb + 1);
-        mx = max_xor32(max_xor16(mx));
-        if (g == 0)
-            smax[w][c] = mx;
-        __syncthreads();
-        mx = __fmul_rn(fmax2(fmax2(smax[0][c], smax[1][c]), fmax2(smax[2][c], smax[3][c])), a.scale_log2);
-        const float nmu = mx == -INFINITY ? 0.f : -mx;
-
-        // ---- p, this wave's level of the sum tree, P^T values to LDS
-        float part[KPW];
-#pragma unroll
-        for (int kl = 0; kl < KPW; ++kl) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s[kl][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kl][i], a.scale_log2, nmu));
-            part[kl] = __fadd_rn(__fadd_rn(s[kl][0], s[kl][1]), __fadd_rn(s[kl][2], s[kl][3]));
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const __bf16 lo = (__bf16)s[kl][2 * h], hi = (__bf16)s[kl][2 * h + 1];
-                spf[w][2 * kl + h][lane] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                                           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-            }
-        }
-        ssum[w][lane] = KPW == 2 ? __fadd_rn(part[0], part[KPW - 1]) : part[0];
-        __syncthreads();
-
-        // ---- l: remaining levels of the tree, then across lanes
-        float l = __fadd_rn(__fadd_rn(ssum[0][lane], ssum[1][lane]), __fadd_rn(ssum[2][lane], ssum[3][lane]));
-        l = sum_xor32(sum_xor16(l));
-
-        // ---- P^T operands of every 32-key step, then P.V for this wave's dims
-        bf16x8 pf[G::NKS];
-#pragma unroll
-        for (int st = 0; st < G::NKS; ++st) {
-            u32x4 u;
-            if (KPW == 2) {
-                u = u32x4{spf[st][0][lane], spf[st][1][lane], spf[st][2][lane], spf[st][3][lane]};
-            } else {
-                u = u32x4{spf[2 * st][0][lane], spf[2 * st][1][lane], spf[2 * st + 1][0][lane], spf[2 * st + 1][1][lane]};
-            }
-            pf[st] = __builtin_bit_cast(bf16x8, u);
-        }
-        float *accp = a.ws_acc + (slot * a.split_cols + col) * D + 4 * g;
-#pragma unroll
-        for (int dl = 0; dl < DPW; ++dl) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int st = 0; st < G::NKS; ++st)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dl][st], pf[st], acc, 0, 0, 0);
-            if (col < ncols) {
-                // head_dim 512: 16 KB of partials per tile (an eighth of the tile's
-                // K/V bytes) stream out during the kernel instead of leaving the
-                // L2 dirty for its end
-                if (D == 512)
-                    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)));
-                else
-                    *reinterpret_cast<f32x4 *>(accp + 16 * (w * DPW + dl)) = acc;
-            }
-        }
-        if (w == 0 && g == 0 && col < ncols) {
-            a.ws_m[slot * a.split_cols + col] = mx;
-            a.ws_l[slot * a.split_cols + col] = l;
-        }
+    }
+    if (w == 0 && g == 0 && c < ncols) {
+        a.ws_m[slot * a.split_cols + c] = mx;
+        a.ws_l[slot * a.split_cols + c] = l;
     }
 }
 
@@ -1168,13 +1160,15 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
 }
 
 // Fold kernel for rows with many columns (split_cols > 16).  Workgroup =
-// (kFoldWideCols consecutive columns, 32-dim slice, kv head, sequence), one
-// wave per column: in rounds of up to 64 tiles, lane t of the wave loads the
-// column's (m, l) of tile t and the wave scans the running max (the same
-// prefix max and the same fold factors as split_fold_kernel); all waves stage
-// the round's acc partials of the workgroup's columns in LDS; then lanes 0-31
-// of each wave run the ACC chain of one dim and lane 32 the L chain, in tile
-// order.  Same operations per (column, dim), so the same bits.
+// (kFoldWideCols consecutive columns, 64-dim slice, kv head, sequence), one
+// wave per column, one dim per lane.  In rounds of up to 64 tiles: lane t
+// loads the column's (m, l) of tile t and every lane loads its dim's acc
+// partials of the round into registers; the wave scans the running max over
+// the lanes (the prefix max of split_fold_kernel) and each lane derives its
+// tile's fold factors; then every lane runs its dim's ACC chain and the
+// column's L chain in tile order, taking tile tt's factors from lane tt
+// (readlane).  Same factors and the same FMA order as split_fold_kernel, so
+// the same bits; no LDS and no barrier.
 constexpr int kFoldWideCols = 8;
 constexpr int kFoldWideTiles = 64;
 
@@ -1182,55 +1176,36 @@ template <int D>
 __global__ __launch_bounds__(64 * kFoldWideCols) void split_fold_wide_kernel(AttnArgs a)
 {
     using G = Geo<D>;
-    constexpr int NSL = D / kFoldSlice;
-    constexpr int NTH = 64 * kFoldWideCols;
-    constexpr int UNITS = kFoldWideCols * kFoldWideTiles * (kFoldSlice / 4);     // 16-byte acc units per round
-    static_assert(UNITS % NTH == 0, "whole units per thread");
-    constexpr int UPT = UNITS / NTH;
-    __shared__ float stage[kFoldWideCols][kFoldWideTiles][kFoldSlice];
-    __shared__ float2 sgh[kFoldWideCols][kFoldWideTiles];
-    __shared__ float sl[kFoldWideCols][kFoldWideTiles];
-
+    constexpr int NSL = D / 64;
     const int slice = blockIdx.x % NSL;
-    const int col0 = (blockIdx.x / NSL) * kFoldWideCols;
+    const int col = (int)(blockIdx.x / NSL) * kFoldWideCols + (int)(threadIdx.x >> 6);
     const int kvh = blockIdx.y;
     const int b = blockIdx.z;
-    const int th = threadIdx.x, lane = th & 63, w = th >> 6;
+    const int lane = threadIdx.x & 63;
     int q0, q_len, seq_len;
     if (!row_ok(a, b, q0, q_len, seq_len))
         return;
     const int ncols = q_len * a.group;
-    if (ncols > a.split_cols || col0 >= ncols)
+    if (ncols > a.split_cols || col >= ncols)      // wave-uniform
         return;
-    const int col = col0 + w;                      // this wave's column (may be past the row's last)
     const int n_tiles = (seq_len + G::T - 1) / G::T;
     const int64_t slot0 = ((int64_t)b * a.num_kv_heads + kvh) * a.max_tiles;
-    const int d0 = slice * kFoldSlice;
+    const int d = slice * 64 + lane;
 
     float M = -INFINITY, L = 0.f, acc = 0.f;
     for (int t0 = 0; t0 < n_tiles; t0 += kFoldWideTiles) {
         const int nt = min(kFoldWideTiles, n_tiles - t0);
-        if (t0 > 0)
-            __syncthreads();                       // the previous round's LDS is read
-        // (m, l) of tile t0 + lane of this wave's column, and the acc units of the round
         float mt = -INFINITY, lt = 0.f;
-        if (lane < nt && col < ncols) {
+        if (lane < nt) {
             const int64_t si = (slot0 + t0 + lane) * a.split_cols + col;
             mt = a.ws_m[si];
             lt = a.ws_l[si];
         }
-        f32x4 v[UPT];
+        float v[kFoldWideTiles];
+        const float *src = a.ws_acc + ((slot0 + t0) * a.split_cols + col) * D + d;
 #pragma unroll
-        for (int r = 0; r < UPT; ++r) {
-            const int u = th + r * NTH;
-            const int q = u % (kFoldSlice / 4);
-            const int tt = (u / (kFoldSlice / 4)) % kFoldWideTiles;
-            const int cc = u / (kFoldSlice / 4) / kFoldWideTiles;
-            v[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (tt < nt && col0 + cc < ncols)
-                v[r] = *reinterpret_cast<const f32x4 *>(a.ws_acc + ((slot0 + t0 + tt) * a.split_cols + col0 + cc) * D +
-                                                        d0 + 4 * q);
-        }
+        for (int tt = 0; tt < kFoldWideTiles; ++tt)
+            v[tt] = tt < nt ? src[(int64_t)tt * a.split_cols * D] : 0.f;
         // running max before each tile (lane = tile), from the running max M of earlier rounds
         float incl = mt;
 #pragma unroll
@@ -1241,42 +1216,23 @@ __global__ __launch_bounds__(64 * kFoldWideCols) void split_fold_wide_kernel(Att
         incl = fmax2(incl, M);
         float excl = __shfl_up(incl, 1, 64);
         excl = lane == 0 ? M : excl;
-        if (lane < nt) {
-            const FoldF f = fold_factors(ref_of(excl), mt);
-            sgh[w][lane] = make_float2(f.gs, f.h);
-            sl[w][lane] = lt;
-        }
-        M = __shfl(incl, 63, 64);
+        const FoldF f = fold_factors(ref_of(excl), mt);
+        M = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
 #pragma unroll
-        for (int r = 0; r < UPT; ++r) {
-            const int u = th + r * NTH;
-            const int q = u % (kFoldSlice / 4);
-            const int tt = (u / (kFoldSlice / 4)) % kFoldWideTiles;
-            const int cc = u / (kFoldSlice / 4) / kFoldWideTiles;
-            *reinterpret_cast<f32x4 *>(&stage[cc][tt][4 * q]) = v[r];
-        }
-        __syncthreads();
-        if (lane < kFoldSlice) {
-#pragma unroll 8
-            for (int tt = 0; tt < nt; ++tt) {
-                const float2 gh = sgh[w][tt];
-                acc = fold1v(acc, stage[w][tt][lane], gh.x, gh.y);
-            }
-        } else if (lane == kFoldSlice) {
-#pragma unroll 8
-            for (int tt = 0; tt < nt; ++tt) {
-                const float2 gh = sgh[w][tt];
-                L = fold1v(L, sl[w][tt], gh.x, gh.y);
+        for (int tt = 0; tt < kFoldWideTiles; ++tt) {
+            if (tt < nt) {
+                const float gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f.gs), tt));
+                const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f.h), tt));
+                const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lt), tt));
+                acc = fold1v(acc, v[tt], gs, h);
+                L = fold1v(L, l, gs, h);
             }
         }
     }
-    L = __shfl(L, kFoldSlice, 64);
-    if (col < ncols && lane < kFoldSlice) {
-        const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
-        a.out[ci.row * a.out_token_stride + (int64_t)ci.head * D + d0 + lane] = finish1(acc, 1.0f / L);
-        if (a.lse && slice == 0 && lane == 0)
-            a.lse[ci.row * a.lse_token_stride + ci.head] = lse_of(ref_of(M), L);
-    }
+    const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
+    a.out[ci.row * a.out_token_stride + (int64_t)ci.head * D + d] = finish1(acc, 1.0f / L);
+    if (a.lse && slice == 0 && lane == 0)
+        a.lse[ci.row * a.lse_token_stride + ci.head] = lse_of(ref_of(M), L);
 }
 
 // ---------------------------------------------------------------- direct K/V tile transfers
@@ -1366,6 +1322,150 @@ __device__ __forceinline__ void db_mask_tail(char *vl, int seq_len, int tile)
         const int hf = (slot >> 5) & 1;                 // the slot's token half (vslot)
         u32x4 *q = reinterpret_cast<u32x4 *>(vl + pg * G::PAGE + slot * 16);
         *q = mask_tokens(*q, hf * 8, valid);
+    }
+}
+
+// ---------------------------------------------------------------- split-KV partials, many columns
+
+// P.V of one 16-column block from zero, per 16-dim block (32-key steps
+// ascending, the same MFMA chain as every other kernel), stored as the
+// tile's acc partial; the next step's V fragments are read while the
+// current step's MFMAs run.
+template <int D, int DG>
+__device__ __forceinline__ void tile_pv_store(const char *vl, const bf16x8 (&pf)[Geo<D>::NKS], float *accp, bool store)
+{
+    using G = Geo<D>;
+    static_assert(G::NDB % DG == 0, "whole groups");
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    auto vaddr = [&](int db, int stp) -> const char * {
+        const int d = 16 * db + c;
+        return vl + (g >> 1) * G::PAGE + vslot(d, g & 1) * 16 + 2 * stp * G::PAGE;
+    };
+#pragma unroll
+    for (int db0 = 0; db0 < G::NDB; db0 += DG) {
+        f32x4 o[DG];
+        bf16x8 vf[DG], vn[DG];
+#pragma unroll
+        for (int d = 0; d < DG; ++d) {
+            o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+            vf[d] = *reinterpret_cast<const bf16x8 *>(vaddr(db0 + d, 0));
+        }
+#pragma unroll
+        for (int stp = 0; stp < G::NKS; ++stp) {
+            if (stp + 1 < G::NKS) {
+#pragma unroll
+                for (int d = 0; d < DG; ++d)
+                    vn[d] = *reinterpret_cast<const bf16x8 *>(vaddr(db0 + d, stp + 1));
+            }
+#pragma unroll
+            for (int d = 0; d < DG; ++d)
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], pf[stp], o[d], 0, 0, 0);
+#pragma unroll
+            for (int d = 0; d < DG; ++d)
+                vf[d] = vn[d];
+        }
+        if (store) {
+#pragma unroll
+            for (int d = 0; d < DG; ++d) {
+                if (D == 512)
+                    __builtin_nontemporal_store(o[d], reinterpret_cast<f32x4 *>(accp + 16 * (db0 + d)));
+                else
+                    *reinterpret_cast<f32x4 *>(accp + 16 * (db0 + d)) = o[d];
+            }
+        }
+    }
+}
+
+// Split-KV partials for rows with many columns (split_cols > 16).
+// Workgroup = (tile, kv head x group of kTileWaves column blocks, sequence).
+// The tile's K and V pages are staged in LDS once (the prefill kernels'
+// transfers and layout); each wave then runs the prefill tile step (tile_qk,
+// tile_stats, P.V) for one 16-column block and stores the tile's (m, l, acc)
+// partials for the fold instead of folding them.  Per column these are the
+// operations of the split-KV partial kernel, so the same bits; there is no
+// exchange between waves and no barrier after the staging.
+
+template <int D>
+__global__ __launch_bounds__(64 * kTileWaves) void split_tile_kernel(AttnArgs a)
+{
+    using G = Geo<D>;
+    constexpr int NWV = kTileWaves;
+    constexpr int HALF = G::NKB * G::PAGE;        // K (or V) part of one tile
+    constexpr int CPP = G::PAGE / 1024;           // 1 KB chunks per page
+    constexpr int CPW = G::NKB * CPP / NWV;       // K (or V) chunks per wave
+    static_assert(CPW % 4 == 0 && CPP % 4 == 0 && (G::NKB * CPP) % NWV == 0, "runs of four chunks per wave");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    char *const kbuf = lds;
+    char *const vbuf = lds + HALF;
+
+    const int tile = blockIdx.x;
+    const int kvh = blockIdx.y % a.num_kv_heads;
+    const int grp = blockIdx.y / a.num_kv_heads;
+    const int b = blockIdx.z;
+    int q0, q_len, seq_len;
+    if (!row_ok(a, b, q0, q_len, seq_len))
+        return;
+    const int ncols = q_len * a.group;
+    if (ncols > a.split_cols || grp * NWV * 16 >= ncols)
+        return;
+    const int n_tiles = (seq_len + G::T - 1) / G::T;
+    if (tile >= n_tiles)
+        return;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+
+    // ---- stage the tile's K and V pages: this wave's chunks of each
+    const int32_t *bt_row = a.block_tables + (int64_t)b * a.bt_stride;
+    const ids_t<G::NKB> blk = tile_blocks<G::NKB>(a, bt_row, tile);
+    auto lds_addr = [](const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p; };
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+        char *const buf = kv ? vbuf : kbuf;
+        const uint16_t *const cache = kv ? a.v_cache : a.k_cache;
+        const int64_t stride = kv ? a.v_block_stride : a.k_block_stride;
+#pragma unroll
+        for (int i = 0; i < CPW; i += 4) {
+            const int ch = wave * CPW + i;
+            const int page = ch / CPP, part = ch % CPP;
+            const int id = __builtin_amdgcn_readfirstlane(blk[page]);     // inside the pool (tile_blocks)
+            const char *src = reinterpret_cast<const char *>(cache + (int64_t)id * stride + (int64_t)kvh * BS * D);
+            const DbOffsets o = db_offsets(page);
+            db_chunks4(src + part * 1024, kv ? o.v : o.k, lds_addr(buf + page * G::PAGE + part * 1024));
+        }
+    }
+    // Q of this wave's column block while the pages land
+    const int cb = grp * NWV + wave;
+    const int col = cb * 16 + c;
+    Cols<D> cols[1];
+    load_q<D>(cols[0], a, col_info(a, col, kvh, q0, q_len, seq_len));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if ((tile + 1) * G::T > seq_len) {
+        db_mask_tail<D, NWV>(vbuf, seq_len, tile);
+        __syncthreads();
+    }
+    if (cb * 16 >= ncols)                           // wave-uniform; no barrier follows
+        return;
+
+    f32x4 sc[1][G::NKB];
+    tile_qk<D, 1>(kbuf, cols, sc);
+    int min_lim = cols[0].lim;
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2)
+        min_lim = min(min_lim, __shfl_xor(min_lim, off, 64));
+    float mx[1], lsum[1];
+    bf16x8 pf[1][G::NKS];
+    if ((tile + 1) * G::T > min_lim)
+        tile_stats<D, 1, true>(sc, cols, tile, a.scale_log2, mx, lsum, pf);
+    else
+        tile_stats<D, 1, false>(sc, cols, tile, a.scale_log2, mx, lsum, pf);
+    const int64_t slot = ((int64_t)b * a.num_kv_heads + kvh) * a.max_tiles + tile;
+    tile_pv_store<D, (D == 128 ? 8 : 4)>(vbuf, pf[0], a.ws_acc + (slot * a.split_cols + col) * D + 4 * g, col < ncols);
+    if (g == 0 && col < ncols) {
+        a.ws_m[slot * a.split_cols + col] = mx[0];
+        a.ws_l[slot * a.split_cols + col] = lsum[0];
     }
 }
 
@@ -2586,20 +2686,27 @@ static hipError_t split_launch(const AttnArgs &a, int max_query_len, hipStream_t
 {
     if (a.max_tiles <= 0 || a.num_seqs <= 0)
         return hipSuccess;
-    // columns a row of this call can have on the split path, in groups of
-    // kSplitGroupBlocks 16-column blocks per workgroup
+    // columns a row of this call can have on the split path
     const int max_cols = (int)min((int64_t)a.split_cols, (int64_t)max_query_len * a.group);
-    const int groups = ((max_cols + 15) / 16 + kSplitGroupBlocks - 1) / kSplitGroupBlocks;
-    const dim3 grid((unsigned)a.max_tiles, (unsigned)(a.num_kv_heads * groups), (unsigned)a.num_seqs);
-    if (fuse)   // one more column of workgroups for the cache write (decode: one column block)
-        hipLaunchKernelGGL((split_partial_kernel<D, true, false>), dim3(grid.x + 1, grid.y, grid.z), dim3(NT), 0, s, a);
-    else if (a.split_cols > kSplitCols)
-        hipLaunchKernelGGL((split_partial_kernel<D, false, true>), grid, dim3(NT), 0, s, a);
-    else
-        hipLaunchKernelGGL((split_partial_kernel<D, false, false>), grid, dim3(NT), 0, s, a);
+    dim3 grid((unsigned)a.max_tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+    if (fuse) {   // one more column of workgroups for the cache write (one column block)
+        hipLaunchKernelGGL((split_partial_kernel<D, true>), dim3(grid.x + 1, grid.y, grid.z), dim3(NT), 0, s, a);
+    } else if (a.split_cols > kSplitCols) {
+        // rows with many columns: tiles staged in LDS, one wave per 16-column block
+        constexpr int LDS_BYTES = 2 * Geo<D>::NKB * Geo<D>::PAGE;
+        const int tgroups = ((max_cols + 15) / 16 + kTileWaves - 1) / kTileWaves;
+        static const hipError_t attr = hipFuncSetAttribute((const void *)split_tile_kernel<D>,
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (attr != hipSuccess)
+            return attr;
+        grid.y = (unsigned)(a.num_kv_heads * tgroups);
+        hipLaunchKernelGGL((split_tile_kernel<D>), grid, dim3(64 * kTileWaves), LDS_BYTES, s, a);
+    } else {
+        hipLaunchKernelGGL((split_partial_kernel<D, false>), grid, dim3(NT), 0, s, a);
+    }
     if (a.split_cols > kSplitCols) {
-        // one fold workgroup per (kFoldWideCols columns, 32-dim slice)
-        const dim3 fgrid((unsigned)((max_cols + kFoldWideCols - 1) / kFoldWideCols * (D / kFoldSlice)),
+        // one fold workgroup per (kFoldWideCols columns, 64-dim slice)
+        const dim3 fgrid((unsigned)((max_cols + kFoldWideCols - 1) / kFoldWideCols * (D / 64)),
                          (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
         hipLaunchKernelGGL((split_fold_wide_kernel<D>), fgrid, dim3(64 * kFoldWideCols), 0, s, a);
     } else {

@@ -196,7 +196,7 @@ int prepare_attention(const kvp_pool *pool, const void *q, int64_t q_token_strid
     // kMaxSplitCols) to the split-KV path as well: the widest limit that fits.
     const bool split_only = (int64_t)max_query_len * G <= kvp::kSplitCols;
     // launch grids: rows in gridDim.z, kv heads x column-block groups in gridDim.y
-    constexpr int kMaxGroups = (kvp::kMaxSplitCols / 16 + kvp::kSplitGroupBlocks - 1) / kvp::kSplitGroupBlocks;
+    constexpr int kMaxGroups = (kvp::kMaxSplitCols / 16 + kvp::kTileWaves - 1) / kvp::kTileWaves;
     if (num_seqs > 65535 || (int64_t)d.num_kv_heads * kMaxGroups > 65535)
         return fail(KVP_ERR_UNSUPPORTED, "paged_attention: num_seqs must be <= 65535 and num_kv_heads <= %d",
                     65535 / kMaxGroups);

@@ -22,10 +22,10 @@ constexpr int tile_tokens(int head_dim) { return head_dim == 128 ? 128 : 64; }
 // rows with at most this many columns always take the split-KV path.
 constexpr int kSplitCols = 16;
 // A larger workspace lets rows with up to kMaxSplitCols columns take the
-// split-KV path too (each partial workgroup then runs up to
-// kSplitGroupBlocks column blocks of its tile).
+// split-KV path too: their partial workgroups stage one KV tile in LDS and
+// run kTileWaves column blocks against it, one per wave.
 constexpr int kMaxSplitCols = 1024;
-constexpr int kSplitGroupBlocks = 4;
+constexpr int kTileWaves = 8;
 
 struct CacheArgs {
     const uint16_t *k, *v;

@@ -1159,80 +1159,110 @@ __global__ __launch_bounds__(NT) void split_fold_kernel(AttnArgs a)
     }
 }
 
+// Register fold of NU (column, 64-dim slice) units of one row by one wave,
+// one dim per lane.  In rounds of up to 64 tiles: lane t loads a unit's
+// (m, l) of tile t and every lane loads its dim's acc partials of the round
+// into registers (all units' loads issued before any is used); the wave scans
+// the running max over the lanes (the prefix max of split_fold_kernel) and
+// each lane derives its tile's fold factors; then every lane runs its dim's
+// ACC chain and the column's L chain in tile order, taking tile tt's factors
+// from lane tt (readlane).  Same factors and the same FMA order as
+// split_fold_kernel, so the same bits; no LDS and no barrier.  on[j] is
+// wave-uniform (a unit past the row's columns is skipped).
+constexpr int kFoldWideTiles = 64;
+
+template <int D, int NU>
+__device__ __forceinline__ void fold_units(const AttnArgs &a, int b, int kvh, int q0, int q_len, int seq_len,
+                                           const int (&col)[NU], const int (&slice)[NU], const bool (&on)[NU])
+{
+    using G = Geo<D>;
+    const int lane = threadIdx.x & 63;
+    const int n_tiles = (seq_len + G::T - 1) / G::T;
+    const int64_t slot0 = ((int64_t)b * a.num_kv_heads + kvh) * a.max_tiles;
+    float M[NU], L[NU], acc[NU];
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+        M[j] = -INFINITY;
+        L[j] = 0.f;
+        acc[j] = 0.f;
+    }
+    for (int t0 = 0; t0 < n_tiles; t0 += kFoldWideTiles) {
+        const int nt = min(kFoldWideTiles, n_tiles - t0);
+        float mt[NU], lt[NU], v[NU][kFoldWideTiles];
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            mt[j] = -INFINITY;
+            lt[j] = 0.f;
+            if (on[j] && lane < nt) {
+                const int64_t si = (slot0 + t0 + lane) * a.split_cols + col[j];
+                mt[j] = a.ws_m[si];
+                lt[j] = a.ws_l[si];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            const float *src = a.ws_acc + ((slot0 + t0) * a.split_cols + col[j]) * D + slice[j] * 64 + lane;
+#pragma unroll
+            for (int tt = 0; tt < kFoldWideTiles; ++tt)
+                v[j][tt] = on[j] && tt < nt ? src[(int64_t)tt * a.split_cols * D] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            // running max before each tile (lane = tile), from the running max M of earlier rounds
+            float incl = mt[j];
+#pragma unroll
+            for (int off = 1; off < 64; off *= 2) {
+                const float o = __shfl_up(incl, off, 64);
+                incl = lane >= off ? fmax2(incl, o) : incl;
+            }
+            incl = fmax2(incl, M[j]);
+            float excl = __shfl_up(incl, 1, 64);
+            excl = lane == 0 ? M[j] : excl;
+            const FoldF f = fold_factors(ref_of(excl), mt[j]);
+            M[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+#pragma unroll
+            for (int tt = 0; tt < kFoldWideTiles; ++tt) {
+                if (tt < nt) {
+                    const float gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f.gs), tt));
+                    const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f.h), tt));
+                    const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lt[j]), tt));
+                    acc[j] = fold1v(acc[j], v[j][tt], gs, h);
+                    L[j] = fold1v(L[j], l, gs, h);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+        if (!on[j])
+            continue;
+        const ColInfo ci = col_info(a, col[j], kvh, q0, q_len, seq_len);
+        a.out[ci.row * a.out_token_stride + (int64_t)ci.head * D + slice[j] * 64 + lane] = finish1(acc[j], 1.0f / L[j]);
+        if (a.lse && slice[j] == 0 && lane == 0)
+            a.lse[ci.row * a.lse_token_stride + ci.head] = lse_of(ref_of(M[j]), L[j]);
+    }
+}
+
 // Fold kernel for rows with many columns (split_cols > 16).  Workgroup =
 // (kFoldWideCols consecutive columns, 64-dim slice, kv head, sequence), one
-// wave per column, one dim per lane.  In rounds of up to 64 tiles: lane t
-// loads the column's (m, l) of tile t and every lane loads its dim's acc
-// partials of the round into registers; the wave scans the running max over
-// the lanes (the prefix max of split_fold_kernel) and each lane derives its
-// tile's fold factors; then every lane runs its dim's ACC chain and the
-// column's L chain in tile order, taking tile tt's factors from lane tt
-// (readlane).  Same factors and the same FMA order as split_fold_kernel, so
-// the same bits; no LDS and no barrier.
+// wave per column: the register fold above, one unit per wave.
 constexpr int kFoldWideCols = 8;
-constexpr int kFoldWideTiles = 64;
 
 template <int D>
 __global__ __launch_bounds__(64 * kFoldWideCols) void split_fold_wide_kernel(AttnArgs a)
 {
-    using G = Geo<D>;
     constexpr int NSL = D / 64;
-    const int slice = blockIdx.x % NSL;
-    const int col = (int)(blockIdx.x / NSL) * kFoldWideCols + (int)(threadIdx.x >> 6);
-    const int kvh = blockIdx.y;
     const int b = blockIdx.z;
-    const int lane = threadIdx.x & 63;
     int q0, q_len, seq_len;
     if (!row_ok(a, b, q0, q_len, seq_len))
         return;
     const int ncols = q_len * a.group;
-    if (ncols > a.split_cols || col >= ncols)      // wave-uniform
+    const int col[1] = {(int)(blockIdx.x / NSL) * kFoldWideCols + (int)(threadIdx.x >> 6)};
+    if (ncols > a.split_cols || col[0] >= ncols)      // wave-uniform
         return;
-    const int n_tiles = (seq_len + G::T - 1) / G::T;
-    const int64_t slot0 = ((int64_t)b * a.num_kv_heads + kvh) * a.max_tiles;
-    const int d = slice * 64 + lane;
-
-    float M = -INFINITY, L = 0.f, acc = 0.f;
-    for (int t0 = 0; t0 < n_tiles; t0 += kFoldWideTiles) {
-        const int nt = min(kFoldWideTiles, n_tiles - t0);
-        float mt = -INFINITY, lt = 0.f;
-        if (lane < nt) {
-            const int64_t si = (slot0 + t0 + lane) * a.split_cols + col;
-            mt = a.ws_m[si];
-            lt = a.ws_l[si];
-        }
-        float v[kFoldWideTiles];
-        const float *src = a.ws_acc + ((slot0 + t0) * a.split_cols + col) * D + d;
-#pragma unroll
-        for (int tt = 0; tt < kFoldWideTiles; ++tt)
-            v[tt] = tt < nt ? src[(int64_t)tt * a.split_cols * D] : 0.f;
-        // running max before each tile (lane = tile), from the running max M of earlier rounds
-        float incl = mt;
-#pragma unroll
-        for (int off = 1; off < 64; off *= 2) {
-            const float o = __shfl_up(incl, off, 64);
-            incl = lane >= off ? fmax2(incl, o) : incl;
-        }
-        incl = fmax2(incl, M);
-        float excl = __shfl_up(incl, 1, 64);
-        excl = lane == 0 ? M : excl;
-        const FoldF f = fold_factors(ref_of(excl), mt);
-        M = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
-#pragma unroll
-        for (int tt = 0; tt < kFoldWideTiles; ++tt) {
-            if (tt < nt) {
-                const float gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f.gs), tt));
-                const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f.h), tt));
-                const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lt), tt));
-                acc = fold1v(acc, v[tt], gs, h);
-                L = fold1v(L, l, gs, h);
-            }
-        }
-    }
-    const ColInfo ci = col_info(a, col, kvh, q0, q_len, seq_len);
-    a.out[ci.row * a.out_token_stride + (int64_t)ci.head * D + d] = finish1(acc, 1.0f / L);
-    if (a.lse && slice == 0 && lane == 0)
-        a.lse[ci.row * a.lse_token_stride + ci.head] = lse_of(ref_of(M), L);
+    const int slice[1] = {(int)(blockIdx.x % NSL)};
+    const bool on[1] = {true};
+    fold_units<D, 1>(a, b, (int)blockIdx.y, q0, q_len, seq_len, col, slice, on);
 }
 
 // ---------------------------------------------------------------- direct K/V tile transfers

@@ -483,7 +483,7 @@ int paged_attention(const kvp_pool *pool, const void *q, int64_t q_token_stride,
                     const int32_t *query_start_loc, int32_t max_query_len, int32_t max_seq_len, float scale,
                     int causal, void *workspace, size_t workspace_bytes, void *stream)
 {
-    kvp::AttnArgs a;
+    kvp::AttnArgs a{};
     AttnPlan plan;
     const int rc = prepare_attention(pool, q, q_token_stride, out, out_token_stride, num_q_heads, num_seqs,
                                      block_tables, block_table_stride, seq_lens, query_start_loc, max_query_len,
@@ -505,7 +505,7 @@ int paged_attention_noalloc(const kvp_pool *pool, const void *q, int64_t q_token
     int rc = scratch_address(&ws);
     if (rc != KVP_OK)
         return rc;
-    kvp::AttnArgs a;
+    kvp::AttnArgs a{};
     AttnPlan plan;
     rc = prepare_attention(pool, q, q_token_stride, out, out_token_stride, num_q_heads, num_seqs, block_tables,
                            block_table_stride, seq_lens, query_start_loc, max_query_len, max_seq_len, scale, causal,
@@ -530,7 +530,7 @@ int paged_attention_lse(const kvp_pool *pool, const void *q, int64_t q_token_str
                         int32_t max_seq_len, float scale, int causal, void *workspace, size_t workspace_bytes,
                         void *stream)
 {
-    kvp::AttnArgs a;
+    kvp::AttnArgs a{};
     AttnPlan plan;
     const int rc = prepare_attention(pool, q, q_token_stride, out, out_token_stride, num_q_heads, num_seqs,
                                      block_tables, block_table_stride, seq_lens, query_start_loc, max_query_len,
@@ -608,7 +608,7 @@ int kvp_decode_step(const kvp_pool *pool, const void *k, const void *v, int64_t 
     int rc = prepare_cache(pool, k, v, num_tokens, k_token_stride, v_token_stride, slot_mapping, ca);
     if (rc != KVP_OK)
         return rc;
-    kvp::AttnArgs a;
+    kvp::AttnArgs a{};
     AttnPlan plan;
     rc = prepare_attention(pool, q, q_token_stride, out, out_token_stride, num_q_heads, num_seqs, block_tables,
                            block_table_stride, seq_lens, query_start_loc, max_query_len, max_seq_len, scale, causal,

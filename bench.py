@@ -395,15 +395,19 @@ def bench_decode_config(name, B, L, Hq, Hkv, D, stream, value_scale=1.0, calls=N
     db = DecodeBench(B, L, Hq, Hkv, D, sets=S, value_scale=value_scale)
     cold, ts = graph_us(db.attention, S, stream)
     warm, _ = graph_us(lambda i: db.attention(0), 50, stream)
+    step, _ = graph_us(db.step_set, S, stream)
     r = rates(cold, nbytes=db.algo_bytes)
     r["groups_us"] = [round(t, 3) for t in ts]
     r["warm"] = rates(warm, nbytes=db.algo_bytes)
+    # kvp_decode_step (the new token's cache write in the partial launch), cold; rate over the
+    # same KV-read bytes as the call
+    r["step"] = rates(step, nbytes=db.algo_bytes)
     r["page_sets"] = S
     r["pool_GB"] = round(S * set_bytes / 1e9, 3)
     del db
     import torch
     torch.cuda.empty_cache()
-    log("%s decode: cold %.2f us/call, warm %.2f us/call" % (name, cold, warm))
+    log("%s decode: cold %.2f us/call, warm %.2f us/call, step %.2f us" % (name, cold, warm, step))
     return r
 
 

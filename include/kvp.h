@@ -197,8 +197,9 @@ int kvp_workspace_bytes(const kvp_pool *pool, int32_t num_q_heads, int32_t num_s
  * Bytes of a workspace that also lets the rows of a mixed batch with up to
  * split_cols columns (q_len * G <= split_cols; split_cols a multiple of 16
  * in [16, 1024]) take the split-KV path: their KV tiles are spread over the
- * chip (one workgroup per tile and group of four 16-column blocks) and their
- * tile states folded in tile order, instead of streaming every tile through
+ * chip (one workgroup per tile and group of up to eight 16-column blocks,
+ * the tile staged in LDS once for all of them) and their tile states folded
+ * in tile order, instead of streaming every tile through
  * one prefill workgroup.  Same bits either way (the fixed schedule of
  * "fix(rocm): stabilize direct paged CK attention for bitwise R/R",
  * Changes); faster when the batch's long-query rows leave the GPU idle and

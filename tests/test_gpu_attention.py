@@ -123,6 +123,15 @@ def test_parity_sweep(case):
     _run_and_compare(w, what="sweep%s" % (case,))
 
 
+def test_decode_many_sequences():
+    """2048 decode rows of 1..400 keys in one call (a grid of 2048 rows of
+    partial and fold workgroups): every output row matches the oracle."""
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(1, 401, size=2048)]
+    w = wl.random_case(61, lens, [1] * len(lens), 8, 2, 128)
+    _run_and_compare(w, what="decode-2048-rows")
+
+
 def test_decode_only_sweep_many_lengths():
     lens = [1, 5, 16, 127, 128, 129, 255, 256, 257, 1000, 4100]
     w = wl.random_case(7, lens, [1] * len(lens), 8, 2, 128)
@@ -185,6 +194,33 @@ def test_mixed_batch_split_and_prefill_paths_agree():
     compare(both, oracle_attention(w, oracle_pool(w)), "mixed batch")
 
 
+def test_mixed_batch_on_a_side_stream_is_complete_for_later_work():
+    """A mixed batch given a workspace, called on a stream other than the
+    default one: work enqueued on that stream after the call (a copy of the
+    output, with no device-wide synchronisation) must see every row, the
+    split-KV rows included, with the bits of the prefill-only run.  Short
+    rows with long KV (a slow split path) beside one small prefill row;
+    three calls in a row."""
+    w = wl.random_case(41, [9000, 12000, 33, 7000], [1, 2, 33, 1], 8, 2, 128)
+    g = GpuCase(w)
+    ref = g.run(use_workspace=False)
+    s = torch.cuda.Stream()
+    before = kvp.kvp_get_counters()["split_kv_launches"]
+    ms, mq = int(w.seq_lens.max()), int(w.max_query_len)
+    copies = []
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            g.out.fill_(-1)
+            kvp.paged_attention(g.pool, g.q, g.out, w.num_q_heads, g.bt, g.seq_lens, g.qsl, mq, ms, w.scale, True,
+                                workspace=g.ws)
+            copies.append(g.out.clone())
+    s.synchronize()
+    assert kvp.kvp_get_counters()["split_kv_launches"] == before + 3
+    for i, c in enumerate(copies):
+        bitwise(host_bits(c), ref, "mixed batch on a helper stream, copy %d" % i)
+
+
 def _decode_step_case(seed, lens, Hq, Hkv, D, new_pos, extra_slots=()):
     """A decode batch plus new K/V rows for the given positions (one per row),
     optionally followed by extra (slot, k, v) rows."""
@@ -239,12 +275,13 @@ def test_decode_step_fused_equals_cache_then_attention(D, Hq, Hkv):
 
 
 @pytest.mark.parametrize("D,Hq,Hkv,split_cols", [(128, 8, 2, 512), (128, 32, 8, 128), (256, 8, 2, 256),
-                                                  (512, 16, 2, 384)])
+                                                  (512, 16, 2, 384), (128, 8, 2, 1024)])
 def test_wide_split_mixed_batch_equals_prefill(D, Hq, Hkv, split_cols):
     """A workspace of kvp_workspace_bytes_split(..., split_cols) sends the
-    rows with q_len * G <= split_cols to the split-KV path (several 16-column
-    blocks per partial workgroup, in groups of four); the others stream
-    through a prefill kernel.  Every row's output and lse equal the
+    rows with q_len * G <= split_cols to the split-KV path (up to eight
+    16-column blocks per partial workgroup against one KV tile staged in
+    LDS, then the register fold); the others stream through a prefill
+    kernel (split_cols 1024 is the widest the library takes).  Every row's output and lse equal the
     prefill-only call (no workspace) bitwise, and match the oracle."""
     G = Hq // Hkv
     lens = [2100, 900, 1500, 3000, 640, 2000]

@@ -151,7 +151,7 @@ int reshape_and_cache(const kvp_pool *pool, const void *k, const void *v, int64_
 int kvp_check_slot_mapping(const kvp_pool *pool, const int64_t *slots, int64_t num_tokens);
 
 /*
- * kv_prepare_block_tables -- page-table metadata prep, host only
+ * kv_prepare_block_tables -- page-table metadata prep on the host
  * ("fix(rocm): stabilize direct paged CK attention for bitwise R/R",
  * Changes: pad page tables to complete KV tiles and sanitise unused
  * columns of active and inactive rows).
@@ -168,6 +168,34 @@ int kvp_check_slot_mapping(const kvp_pool *pool, const int64_t *slots, int64_t n
  */
 int kv_prepare_block_tables(const kvp_pool *pool, const int32_t *block_tables, int32_t num_seqs,
                             int32_t width, const int32_t *seq_lens, int32_t *out);
+
+/*
+ * kv_prepare_block_tables_device -- the same preparation for a table that
+ * is already in device memory, on `stream`, with no host copy and no
+ * synchronisation, so a captured graph can replay it with new tables
+ * ("fix(rocm): stabilize direct paged CK attention for bitwise R/R",
+ * Changes: pad page tables to complete KV tiles, sanitise unused columns of
+ * active and inactive rows, inactive graph rows).
+ *   block_tables  device, [num_seqs][width] int32 (row stride `width`)
+ *   seq_lens      device, [num_seqs] int32
+ *   out           device, [num_seqs][kvp_padded_width(width)] int32; must
+ *                 not overlap block_tables
+ *   status        device int32 or NULL.  The checks of the host version
+ *                 cannot fail the call here; instead the kernel ORs bits
+ *                 into *status for rows the host version would reject
+ *                 (1: negative seq_len, read as 0; 2: more than `width`
+ *                 pages, the extra ones dropped; 4: a kept entry outside
+ *                 [0, num_blocks), written as block 0), so every later
+ *                 kernel stays inside the pool.  The caller clears *status
+ *                 beforehand and reads it whenever it synchronises.
+ * For every table the host version accepts, `out` receives exactly the
+ * host version's values.
+ * Errors: INVALID_ARGUMENT (null pointer, negative size, overlapping
+ * buffers), HIP (launch failure).
+ */
+int kv_prepare_block_tables_device(const kvp_pool *pool, const int32_t *block_tables, int32_t num_seqs,
+                                   int32_t width, const int32_t *seq_lens, int32_t *out, int32_t *status,
+                                   void *stream);
 
 /* Width a prepared table has: width rounded up to a multiple of 8 pages,
  * i.e. whole 128-token KV tiles ("fix(rocm): stabilize direct paged CK

@@ -64,6 +64,7 @@ def load_library(path: str = LIB_PATH):
         "kv_pool_span_bytes": ([P, ctypes.POINTER(I64)], I),
         "reshape_and_cache": ([P, P, P, I64, I64, I64, P, P], I),
         "kv_prepare_block_tables": ([P, P, ctypes.c_int32, ctypes.c_int32, P, P], I),
+        "kv_prepare_block_tables_device": ([P, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P], I),
         "kvp_padded_width": ([ctypes.c_int32], ctypes.c_int32),
         "kvp_check_slot_mapping": ([P, P, I64], I),
         "kvp_workspace_bytes": ([P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(SZ)], I),
@@ -208,6 +209,20 @@ def kv_prepare_block_tables(pool: KVPool, block_tables, seq_lens) -> np.ndarray:
     _check(load_library().kv_prepare_block_tables(pool.handle, bt.ctypes.data_as(ctypes.c_void_p), B, W,
                                                   sl.ctypes.data_as(ctypes.c_void_p),
                                                   out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def kv_prepare_block_tables_device(pool: KVPool, block_tables, seq_lens, out=None, status=None, stream=None):
+    """The same on the device: block_tables [B, W] and seq_lens [B] int32 device tensors ->
+    out [B, padded W] int32 device tensor (allocated here when not given), on the stream.
+    status: an optional device int32 tensor of one element into which the kernel ORs the
+    problem bits of rows the host version would reject (see include/kvp.h)."""
+    import torch
+    B, W = int(block_tables.shape[0]), int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty((B, kvp_padded_width(W)), dtype=torch.int32, device=block_tables.device)
+    _check(load_library().kv_prepare_block_tables_device(pool.handle, _ptr(block_tables), B, W, _ptr(seq_lens),
+                                                         _ptr(out), _ptr(status), _stream(stream)))
     return out
 
 

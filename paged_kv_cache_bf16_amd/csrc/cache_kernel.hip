@@ -132,6 +132,59 @@ hipError_t launch_reshape_and_cache(const CacheArgs &a, hipStream_t s, uint64_t 
     return hipGetLastError();
 }
 
+// Block-table preparation on the device: one thread per output entry of the
+// padded table.  Row b keeps its first ceil(seq_len / 16) entries and repeats
+// its last kept entry in every later column (0 for a row without pages);
+// entries outside the pool become block 0.  Rows the host preparation would
+// reject set bits in *status (1: negative seq_len, read as 0; 2: more pages
+// than the row has columns, the extra ones dropped; 4: a kept entry outside
+// the pool).
+__global__ __launch_bounds__(256) void table_kernel(TableArgs a)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)a.num_seqs * a.padded_width)
+        return;
+    const int b = (int)(i / a.padded_width);
+    const int c = (int)(i % a.padded_width);
+    int64_t sl = a.seq_lens[b];
+    int flags = 0;
+    if (sl < 0) {
+        flags |= 1;
+        sl = 0;
+    }
+    int64_t np = (sl + KVP_BLOCK_SIZE - 1) / KVP_BLOCK_SIZE;
+    if (np > a.width) {
+        flags |= 2;
+        np = a.width;
+    }
+    const int32_t *src = a.block_tables + (int64_t)b * a.width;
+    int32_t v = 0;
+    if (np > 0) {
+        const int32_t id = src[c < np ? c : np - 1];
+        const bool bad = id < 0 || (int64_t)id >= a.num_blocks;
+        if (bad && c < np)
+            flags |= 4;
+        v = bad ? 0 : id;
+    }
+    a.out[i] = v;
+    if (flags && a.status)
+        atomicOr(a.status, flags);
+}
+
+hipError_t launch_prepare_tables(const TableArgs &a, hipStream_t s, uint64_t *blocks)
+{
+    const int64_t n = (int64_t)a.num_seqs * a.padded_width;
+    const int64_t g = (n + 255) / 256;
+    *blocks = 0;
+    if (g <= 0)
+        return hipSuccess;
+    if (g > 0x7fffffff)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(table_kernel, dim3((unsigned)g), dim3(256), 0, s, a);
+    *blocks = (uint64_t)g;
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s, uint64_t *blocks)
 {
     const int64_t n16 = (int64_t)(bytes / 16);

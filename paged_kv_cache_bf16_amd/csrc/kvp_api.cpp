@@ -365,6 +365,34 @@ int reshape_and_cache(const kvp_pool *pool, const void *k, const void *v, int64_
     return launch_cache(a, stream);
 }
 
+int kv_prepare_block_tables_device(const kvp_pool *pool, const int32_t *block_tables, int32_t num_seqs,
+                                   int32_t width, const int32_t *seq_lens, int32_t *out, int32_t *status,
+                                   void *stream)
+{
+    if (!pool)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_prepare_block_tables_device: null pool");
+    if (num_seqs < 0 || width < 0)
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_prepare_block_tables_device: negative size");
+    if (num_seqs == 0)
+        return ok();
+    if (!seq_lens || !out || (width > 0 && !block_tables))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_prepare_block_tables_device: null argument");
+    const int32_t wp = kvp_padded_width(width);
+    if (width > 0) {
+        const uintptr_t i0 = (uintptr_t)block_tables, i1 = i0 + (uintptr_t)num_seqs * width * 4;
+        const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (uintptr_t)num_seqs * wp * 4;
+        if (i0 < o1 && o0 < i1)
+            return fail(KVP_ERR_INVALID_ARGUMENT, "kv_prepare_block_tables_device: out overlaps block_tables");
+    }
+    kvp::TableArgs a{block_tables, seq_lens, out, status, num_seqs, width, wp, pool->d.num_blocks};
+    uint64_t blocks = 0;
+    hipError_t e = kvp::launch_prepare_tables(a, (hipStream_t)stream, &blocks);
+    if (e != hipSuccess)
+        return hip_fail(e, "kv_prepare_block_tables_device launch");
+    g_last_grid = blocks;
+    return ok();
+}
+
 int32_t kvp_padded_width(int32_t width)
 {
     if (width <= 0)

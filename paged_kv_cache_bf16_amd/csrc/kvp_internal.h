@@ -85,6 +85,15 @@ hipError_t launch_split_kv_fused(const AttnArgs &a, int head_dim, int max_query_
 hipError_t launch_prefill(const AttnArgs &a, int head_dim, int max_query_len, hipStream_t s, uint64_t *blocks);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s, uint64_t *blocks);
 
+// Block-table preparation on the device (kv_prepare_block_tables_device).
+struct TableArgs {
+    const int32_t *block_tables, *seq_lens;
+    int32_t *out, *status;
+    int32_t num_seqs, width, padded_width;
+    int64_t num_blocks;
+};
+hipError_t launch_prepare_tables(const TableArgs &a, hipStream_t s, uint64_t *blocks);
+
 // Merge of two (output, lse) results over disjoint key sets; rows are
 // [pairs][head_dim] BF16, lse [pairs] FP32 (lse may be null).
 struct MergeArgs {

@@ -179,6 +179,25 @@ def test_reshape_rejects_before_launch(lib, args, code):
     lib.kv_pool_destroy(h)
 
 
+@pytest.mark.parametrize("args", [
+    dict(pool=None), dict(B=-1), dict(W=-1), dict(bt=None), dict(sl=None), dict(out=None),
+    dict(out=0x30000010),                     # overlaps the input table
+    dict(bt=0x32000010),                      # the input table overlaps the output
+])
+def test_prepare_tables_device_rejects_before_launch(lib, args):
+    """kv_prepare_block_tables_device: bad arguments fail before anything is
+    queued (the pointers are never dereferenced); an empty batch is a no-op."""
+    rc, h = create(lib)
+    a = dict(pool=h, bt=0x30000000, B=3, W=10, sl=0x31000000, out=0x32000000)
+    a.update(args)
+    kvp.kvp_reset_counters()
+    f = lib.kv_prepare_block_tables_device
+    assert f(a["pool"], a["bt"], a["B"], a["W"], a["sl"], a["out"], None, None) == kvp.KVP_ERR_INVALID_ARGUMENT
+    assert kvp.kvp_get_counters()["last_grid_blocks"] == 0
+    assert f(h, None, 0, 10, None, None, None, None) == 0
+    lib.kv_pool_destroy(h)
+
+
 def test_workspace_bytes_scales_with_tiles(lib):
     rc, h = create(lib)
     pool = kvp.KVPool(h, make_desc(), None)

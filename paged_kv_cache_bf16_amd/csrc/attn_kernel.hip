@@ -766,11 +766,20 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
     }
     // The tile's block-table entries are always inside the padded row
     // (tile < max_tiles), so they are fetched together with the row's
-    // metadata instead of after it.
+    // metadata instead of after it: the four loads are issued at once and
+    // the empty asm statement, which takes all of them as inputs, keeps the
+    // compiler from sinking the block-id load below the row checks or
+    // ordering the metadata loads one after another (it computes nothing).
     const int32_t *bt_row = a.block_tables + (int64_t)b * a.bt_stride;
-    const ids_t<G::NKB> blk = tile_blocks<G::NKB>(a, bt_row, tile);
-    int q0, q_len, seq_len;
-    if (!row_ok(a, b, q0, q_len, seq_len))
+    const ids_t<G::NKB> raw = *reinterpret_cast<const ids_t<G::NKB> *>(bt_row + tile * G::NKB);
+    const int r_q0 = a.qsl[b], r_q1 = a.qsl[b + 1], r_sl = a.seq_lens[b];
+    asm volatile("" ::"s"(raw[0]), "s"(raw[G::NKB - 1]), "s"(r_q0), "s"(r_q1), "s"(r_sl));
+    ids_t<G::NKB> blk;
+#pragma unroll
+    for (int i = 0; i < G::NKB; ++i)
+        blk[i] = (raw[i] < 0 || (int64_t)raw[i] >= a.num_blocks) ? 0 : raw[i];
+    const int q0 = r_q0, q_len = r_q1 - r_q0, seq_len = r_sl;
+    if (!(q_len > 0 && q_len <= seq_len && seq_len <= a.max_seq_len && q0 >= 0))    // as row_ok
         return;
     const int ncols = q_len * a.group;
     if (ncols > a.split_cols)
@@ -906,16 +915,32 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
             }
         }
     }
+    // V of keys >= seq_len is zeroed; only the tile holding key seq_len - 1
+    // has such keys (a wave-uniform branch, so full tiles skip the masks)
     bf16x8 vf[DPW][G::NKS];
+    if ((tile + 1) * G::T > seq_len) {
 #pragma unroll
-    for (int st = 0; st < G::NKS; ++st) {
-        const int valid = seq_len - (tile * G::NKB + 2 * st + (g >> 1)) * BS;
+        for (int st = 0; st < G::NKS; ++st) {
+            const int valid = seq_len - (tile * G::NKB + 2 * st + (g >> 1)) * BS;
 #pragma unroll
-        for (int dl = 0; dl < DPW; ++dl)
-            vf[dl][st] = __builtin_bit_cast(bf16x8, valid >= BS ? vraw[dl][st] : mask_tokens(vraw[dl][st], 8 * (g & 1), valid));
+            for (int dl = 0; dl < DPW; ++dl)
+                vf[dl][st] = __builtin_bit_cast(bf16x8, valid >= BS ? vraw[dl][st]
+                                                                    : mask_tokens(vraw[dl][st], 8 * (g & 1), valid));
+        }
+    } else {
+#pragma unroll
+        for (int st = 0; st < G::NKS; ++st)
+#pragma unroll
+            for (int dl = 0; dl < DPW; ++dl)
+                vf[dl][st] = __builtin_bit_cast(bf16x8, vraw[dl][st]);
     }
 
-    // ---- S for this wave's key blocks; scale, mask, wave max
+    // ---- S for this wave's key blocks; scale, mask, wave max.  Scores are
+    // masked only in a tile that reaches past the smallest key limit of the
+    // row's columns (the first query's); a column past ncols is never
+    // stored, and no column's output depends on another column's scores.
+    const int lim_min = a.causal ? seq_len - q_len + 1 : seq_len;
+    const bool smask = (tile + 1) * G::T > lim_min;
     f32x4 s[KPW];
     float mx = -INFINITY;
 #pragma unroll
@@ -927,10 +952,13 @@ __global__ __launch_bounds__(NT) void split_partial_kernel(AttnArgs a)
                                                           0, 0, 0);
         const int kb = w * KPW + kl;
         const int st = kb >> 1, e = kb & 1;
+        s[kl] = acc;
+        if (smask) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = tile * G::T + 32 * st + 8 * g + 4 * e + i;
-            s[kl][i] = key < cols.lim ? acc[i] : -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+                const int key = tile * G::T + 32 * st + 8 * g + 4 * e + i;
+                s[kl][i] = key < cols.lim ? acc[i] : -INFINITY;
+            }
         }
         mx = fmax2(mx, fmax2(fmax2(s[kl][0], s[kl][1]), fmax2(s[kl][2], s[kl][3])));
     }

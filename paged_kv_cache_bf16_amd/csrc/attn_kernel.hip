@@ -330,6 +330,41 @@ __device__ __forceinline__ bool row_ok(const AttnArgs &a, int b, int &q0, int &q
     return q_len > 0 && q_len <= seq_len && seq_len <= a.max_seq_len && q0 >= 0;
 }
 
+// Prefill workgroup -> (sequence b, kv head, column-group index cgi; cgi 0 is
+// the row's heaviest (latest) column group).  Workgroups go to the 8 XCDs
+// round-robin (XCD = blockIdx.x % 8), and one XCD's workgroups share its L2.
+// When the rows' column groups fit in one XCD's share of the grid, each XCD
+// takes a contiguous run of (row, column group) pairs, so a row's tiles are
+// read through one L2.  When a row has more column groups than that share
+// (few rows, long causal rows), a contiguous run would give some XCDs only
+// the heavy column groups and others only the light ones, so the pairs are
+// dealt out column group by column group instead: XCD x takes every 8th
+// pair, heaviest first, and with a row count dividing 8 it stays on one row.
+// Returns false for the grid's padding workgroups.
+__device__ __forceinline__ bool wg_slot(const AttnArgs &a, int &b, int &kvh, int &cgi)
+{
+    const int rows = a.num_seqs * a.num_kv_heads;
+    const int n = rows * a.col_groups;
+    const int per = (n + 7) / 8;
+    int r;
+    if (a.col_groups > per) {
+        const int j = (int)blockIdx.x;
+        if (j >= n)
+            return false;
+        r = j % rows;
+        cgi = j / rows;
+    } else {
+        const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+        if (j >= n)
+            return false;
+        r = j / a.col_groups;
+        cgi = j % a.col_groups;
+    }
+    kvh = r % a.num_kv_heads;
+    b = r / a.num_kv_heads;
+    return true;
+}
+
 // ---------------------------------------------------------------- joint tile step (prefill)
 
 // P.V for every 16-dim block of CB column blocks, each result folded into
@@ -1575,14 +1610,9 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     char *const vbuf = lds + HALF;
     int32_t *const ids = reinterpret_cast<int32_t *>(lds + 2 * HALF);     // [2][NKB]
 
-    const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
-    const int per = (n + 7) / 8;
-    const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (j >= n)
+    int b, kvh, cgi;
+    if (!wg_slot(a, b, kvh, cgi))
         return;
-    const int cgi = j % a.col_groups;
-    const int kvh = (j / a.col_groups) % a.num_kv_heads;
-    const int b = j / (a.col_groups * a.num_kv_heads);
     const int cg = a.col_groups - 1 - cgi;           // heaviest (latest) columns first
 
     int q0, q_len, seq_len;
@@ -1713,14 +1743,9 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     extern __shared__ __attribute__((aligned(16))) char lds[];
     int32_t *const ids = reinterpret_cast<int32_t *>(lds + 4 * HALF);     // [2][NKB]
 
-    const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
-    const int per = (n + 7) / 8;
-    const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (j >= n)
+    int b, kvh, cgi;
+    if (!wg_slot(a, b, kvh, cgi))
         return;
-    const int cgi = j % a.col_groups;
-    const int kvh = (j / a.col_groups) % a.num_kv_heads;
-    const int b = j / (a.col_groups * a.num_kv_heads);
     const int cg = a.col_groups - 1 - cgi;           // heaviest (latest) columns first
 
     int q0, q_len, seq_len;
@@ -2080,14 +2105,9 @@ __device__ __forceinline__ WsSetup ws_setup(const AttnArgs &a)
 {
     WsSetup w{};
     w.run = false;
-    const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
-    const int per = (n + 7) / 8;
-    const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (j >= n)
+    int cgi;
+    if (!wg_slot(a, w.b, w.kvh, cgi))
         return w;
-    const int cgi = j % a.col_groups;
-    w.kvh = (j / a.col_groups) % a.num_kv_heads;
-    w.b = j / (a.col_groups * a.num_kv_heads);
     w.cg = a.col_groups - 1 - cgi;                  // heaviest (latest) columns first
     if (!row_ok(a, w.b, w.q0, w.q_len, w.seq_len))
         return w;
@@ -2262,14 +2282,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     int32_t *const ids = reinterpret_cast<int32_t *>(lds + 4 * HALF);                   // [2][NKB]
     StageX<D> *const xs = reinterpret_cast<StageX<D> *>(lds + 4 * HALF + 2 * G::NKB * 4);   // [4]
 
-    const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
-    const int per = (n + 7) / 8;
-    const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (j >= n)
+    int b, kvh, cgi;
+    if (!wg_slot(a, b, kvh, cgi))
         return;
-    const int cgi = j % a.col_groups;
-    const int kvh = (j / a.col_groups) % a.num_kv_heads;
-    const int b = j / (a.col_groups * a.num_kv_heads);
     const int cg = a.col_groups - 1 - cgi;           // heaviest (latest) columns first
     int q0, q_len, seq_len;
     if (!row_ok(a, b, q0, q_len, seq_len))
@@ -2444,14 +2459,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     char *const kbuf0 = lds, *const kbuf1 = lds + HALF;
     char *const vbuf0 = lds + 2 * HALF, *const vbuf1 = lds + 3 * HALF;
 
-    const int n = a.num_seqs * a.num_kv_heads * a.col_groups;
-    const int per = (n + 7) / 8;
-    const int j = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (j >= n)
+    int b, kvh, cgi;
+    if (!wg_slot(a, b, kvh, cgi))
         return;
-    const int cgi = j % a.col_groups;
-    const int kvh = (j / a.col_groups) % a.num_kv_heads;
-    const int b = j / (a.col_groups * a.num_kv_heads);
     const int cg = a.col_groups - 1 - cgi;
 
     int q0, q_len, seq_len;

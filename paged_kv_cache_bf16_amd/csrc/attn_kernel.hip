@@ -2259,7 +2259,8 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
 // fold on every tile: gs is 1 unless the reference moved, and ACC * 1 is
 // exact); the two waves of a SIMD are a stage apart, so one's MFMAs fill the
 // other's softmax.  K and V tiles have two LDS buffers each (K(t+1) and V(t)
-// load while K(t) and V(t-1) are read), two barriers per tile.  64 columns
+// load while K(t) and V(t-1) are read; the consumers copy V(t), the
+// producers K(t+1)), two barriers per tile.  64 columns
 // per workgroup, for grids that leave CUs idle with more columns per
 // workgroup.
 template <int D>
@@ -2320,16 +2321,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 
     auto lds_addr = [](const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) char *)p; };
     auto stage = [&](int tile) { return lds + (tile & 1) * 2 * HALF; };
-    // this wave's chunks of the K (or V) part of `tile`
-    auto issue = [&](bool is_k, int tile) {
+    // Chunks of the K (or V) part of `tile` copied by issuing wave iw of NI
+    // (all eight waves for the first K tile, one role's four waves later).
+    auto issue = [&](bool is_k, int tile, int iw, auto ni) {
+        constexpr int NI = decltype(ni)::value;
+        constexpr int CPI = G::NKB * CPP / NI;       // chunks per issuing wave
         char *const buf = stage(tile) + (is_k ? 0 : HALF);
         const uint16_t *const cache = is_k ? a.k_cache : a.v_cache;
         const int64_t stride = is_k ? a.k_block_stride : a.v_block_stride;
         const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
-        static_assert(CPW % 4 == 0 && CPP % 4 == 0, "runs of four chunks");
+        static_assert(CPI % 4 == 0 && CPP % 4 == 0 && CPI * NI == G::NKB * CPP, "runs of four chunks");
 #pragma unroll
-        for (int i = 0; i < CPW; i += 4) {
-            const int ch = wave * CPW + i;
+        for (int i = 0; i < CPI; i += 4) {
+            const int ch = iw * CPI + i;
             const int page = ch / CPP, part = ch % CPP;
             int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
             id = (uint32_t)id < nb ? id : 0;                  // ids outside the pool read block 0
@@ -2349,19 +2353,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
         fetch_ids(1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    issue(true, 0);
+    issue(true, 0, wave, std::integral_constant<int, NWV>{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // step t: the producer computes tile t, the consumer tile t - 1.  Each
     // role runs its own copy of the step loop, with the same barriers in the
     // same order, so the two roles' values never meet at a join.
+    // K(t+1) and V(t) go into buffers last read in step t - 1.  A wave
+    // waits while the CU's memory pipeline takes its transfer instructions
+    // (about 16 cycles per 1 KB chunk for the whole CU), so the consumers copy
+    // V(t) at the start of the step and the producers copy K(t+1) after their
+    // QK, rather than all eight waves copying both at the start.
     auto step_head = [&](int t) {
-        // K(t+1) and V(t) go into buffers last read in step t - 1
-        if (t + 1 <= last)
-            issue(true, t + 1);
-        if (t <= last)
-            issue(false, t);
+        if (!producer && t <= last)
+            issue(false, t, wave - 4, std::integral_constant<int, 4>{});
         // V(t-1) of a tile that reaches seq_len: zero its keys >= seq_len
         if (t >= 1 && t * G::T > seq_len) {
             db_mask_tail<D, NWV>(stage(t - 1) + HALF, seq_len, t - 1);
@@ -2374,9 +2380,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
             const bool work = active && t <= last;
             bf16x8 pf[1][G::NKS];
             FoldF f[1];
-            if (work) {
-                f32x4 sc[1][G::NKB];
+            f32x4 sc[1][G::NKB];
+            if (work)
                 tile_qk<D, 1>(stage(t), cols, sc);
+            if (t + 1 <= last)
+                issue(true, t + 1, wave, std::integral_constant<int, 4>{});
+            if (work) {
                 if ((t + 1) * G::T > min_lim)
                     prefill_softmax_stats<D, 1, true>(sc, cols, t, a.scale_log2, st, pf, f);
                 else

@@ -372,9 +372,16 @@ __device__ __forceinline__ bool wg_slot(const AttnArgs &a, int &b, int &kvh, int
 // where needed).  The V fragments of block db+1 are read while the MFMAs of
 // block db run, and block db is folded after the MFMAs of block db+1 are
 // issued, so neither the LDS latency nor the MFMA latency is exposed.
-template <int D, int CB>
+// Called after each 16-dim (resp. key) block's MFMAs of the two functions
+// below, with the block index: lets a caller spread other instructions
+// (transfers) over the MFMA loop.  The default does nothing.
+struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <int D, int CB, class Hook = NoHook>
 __device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS],
-                                           const FoldF (&f)[CB], State<D> (&st)[CB])
+                                           const FoldF (&f)[CB], State<D> (&st)[CB], Hook hook = Hook{})
 {
     using G = Geo<D>;
     const int lane = threadIdx.x & 63;
@@ -425,6 +432,7 @@ __device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB
             __builtin_amdgcn_sched_group_barrier(0x100, G::NKS, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, G::NKS * CB, 0);
         __builtin_amdgcn_sched_barrier(0);
+        hook(db);
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
@@ -434,8 +442,9 @@ __device__ __forceinline__ void prefill_pv(const char *vl, const bf16x8 (&pf)[CB
 }
 
 // Phase 1 of the tile step: S^T = K . Q^T for every column block.
-template <int D, int CB>
-__device__ __forceinline__ void prefill_qk(const char *kl, const Cols<D> (&cols)[CB], f32x4 (&s)[CB][Geo<D>::NKB])
+template <int D, int CB, class Hook = NoHook>
+__device__ __forceinline__ void prefill_qk(const char *kl, const Cols<D> (&cols)[CB], f32x4 (&s)[CB][Geo<D>::NKB],
+                                           Hook hook = Hook{})
 {
     using G = Geo<D>;
     const int lane = threadIdx.x & 63;
@@ -481,6 +490,7 @@ __device__ __forceinline__ void prefill_qk(const char *kl, const Cols<D> (&cols)
             __builtin_amdgcn_sched_group_barrier(0x100, G::NDS, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, G::NDS * CB, 0);
         __builtin_amdgcn_sched_barrier(0);
+        hook(kb);
     }
 }
 
@@ -2449,10 +2459,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 // the halves.
 //   slot 1: A softmax(t)                 | B P.V(t-1), QK(t)
 //   slot 2: A P.V(t), QK(t+1)            | B softmax(t)
-// K and V tiles have two LDS buffers each.  At the start of slot 2 of
-// iteration t the waves issue K(t+2) and V(t+1) into the buffers that slot 1
-// released (K(t), V(t-1)); they are waited for before the barrier that ends
-// slot 1 of iteration t+1, one slot before their first use.  P of a wave is
+// K and V tiles have two LDS buffers each.  During slot 2 of iteration t the
+// waves of group A copy K(t+2) and V(t+1) into the buffers that slot 1
+// released (K(t), V(t-1)), one 1 KB chunk after every eight of their MFMAs:
+// a wave waits while the CU's memory pipeline takes its transfer
+// instructions (about 16 cycles per chunk for the whole CU), and spread over
+// the slot no wave queues behind the others.  The copies are waited for
+// before the barrier that ends slot 1 of iteration t+1, one slot before
+// their first use.  P of a wave is
 // kept in the register space of its scores (the two are never live together
 // in one wave).
 template <int D, int CB>
@@ -2524,18 +2538,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         issue_k(kbuf0, id0);
         issue_v(vbuf0, id0);
     }
-    int id_v = 0;                                     // block id of tile t+1 (for V(t+1))
-    if (last >= 1) {
-        id_v = __builtin_amdgcn_readfirstlane(db_load_id(bt_row, 1));
-        issue_k(kbuf1, id_v);
-    }
-    int id_next = db_load_id(bt_row, min(2, last));   // tile t+2, landed by slot 2
+    if (last >= 1)
+        issue_k(kbuf1, __builtin_amdgcn_readfirstlane(db_load_id(bt_row, 1)));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // Between the two slots of iteration t (every wave): the transfers of
-    // slot 2 of t-1 have landed; the tail tile's V is masked; K(t+2), V(t+1)
-    // are issued into the buffers slot 1 released.
+    // slot 2 of t-1 have landed; the tail tile's V is masked.
     auto mid = [&](int t) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -2543,13 +2552,44 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             db_mask_tail<D, NWV>(vbuf(t), seq_len, t);
             __syncthreads();
         }
-        const int id_k = __builtin_amdgcn_readfirstlane(id_next);
-        id_next = db_load_id(bt_row, min(t + 3, last));
-        if (t + 2 <= last)
-            issue_k(kbuf(t), id_k);
-        if (t + 1 <= last)
-            issue_v(vbuf(t + 1), id_v);
-        id_v = id_k;
+    };
+    // Group A wave wa copies pages 2 wa and 2 wa + 1 of K(t+2) and V(t+1)
+    // during its MFMA slot of iteration t.  Their block ids are read at the
+    // top of the iteration with scalar loads (the table is read through the
+    // constant address space, so the compiler emits s_load and its wait).
+    // K(t+2) is copied even past the last tile, from the last tile's pages
+    // into kbuf(t), which no wave reads after that slot (no branch in the
+    // MFMA loop).
+    static_assert(G::NKB == 8 && G::PAGE == 4096, "two pages of four chunks per group-A wave");
+    const int wa = wave & 3;
+    struct CpIds {
+        int k0, k1, v0, v1;
+    };
+    using cint = const __attribute__((address_space(4))) int32_t;
+    auto cp_ids = [&](int t) {
+        CpIds r;
+        const int tk = min(t + 2, last), tv = min(t + 1, last);
+        cint *const tb = (cint *)bt_row;
+        r.k0 = tb[tk * 8 + 2 * wa];
+        r.k1 = tb[tk * 8 + 2 * wa + 1];
+        r.v0 = tb[tv * 8 + 2 * wa];
+        r.v1 = tb[tv * 8 + 2 * wa + 1];
+        return r;
+    };
+    const uint32_t nbk = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+    auto cp_chunk = [&](const CpIds &r, int t, bool is_k, int c) {   // c = 0..7: page 2 wa + c / 4, chunk c % 4
+        const int p = 2 * wa + c / 4, i = c % 4;
+        int id = is_k ? (c < 4 ? r.k0 : r.k1) : (c < 4 ? r.v0 : r.v1);
+        id = (uint32_t)id < nbk ? id : 0;
+        const uint16_t *const cache = is_k ? a.k_cache : a.v_cache;
+        const int64_t stride = is_k ? a.k_block_stride : a.v_block_stride;
+        const char *base = reinterpret_cast<const char *>(cache + (int64_t)id * stride + (int64_t)kvh * BS * D);
+        const DbOffsets o = db_offsets(p);
+        char *const dst = (is_k ? kbuf(t) : vbuf(t + 1)) + p * G::PAGE;
+        const uint32_t m0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)dst;
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%2"
+                     :
+                     : "v"(is_k ? o.k : o.v), "s"(base), "i"(i * 1024), "{m0}"(m0));
     };
 
     // The two groups run separate loops with the same barrier sequence
@@ -2564,13 +2604,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int t = 0; t < last; ++t) {
             bf16x8 pf[CB][G::NKS];
             FoldF f[CB];
+            const CpIds ci = cp_ids(t);
             if (active)
                 softmax(t, sc, pf, f);                         // slot 1
             mid(t);
             __builtin_amdgcn_s_setprio(1);
             if (active) {                                      // slot 2
-                prefill_pv<D, CB>(vbuf(t), pf, f, st);
-                prefill_qk<D, CB>(kbuf(t + 1), cols, sc);
+                prefill_pv<D, CB>(vbuf(t), pf, f, st, [&](int db) { cp_chunk(ci, t, false, db); });
+                prefill_qk<D, CB>(kbuf(t + 1), cols, sc, [&](int kb) { cp_chunk(ci, t, true, kb); });
+            } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    cp_chunk(ci, t, false, c);
+                    cp_chunk(ci, t, true, c);
+                }
             }
             __builtin_amdgcn_s_setprio(0);
             __syncthreads();

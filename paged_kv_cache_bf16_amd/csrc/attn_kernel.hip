@@ -372,9 +372,10 @@ __device__ __forceinline__ bool wg_slot(const AttnArgs &a, int &b, int &kvh, int
 // where needed).  The V fragments of block db+1 are read while the MFMAs of
 // block db run, and block db is folded after the MFMAs of block db+1 are
 // issued, so neither the LDS latency nor the MFMA latency is exposed.
-// Called after each 16-dim (resp. key) block's MFMAs of the two functions
-// below, with the block index: lets a caller spread other instructions
-// (transfers) over the MFMA loop.  The default does nothing.
+// Hook of the QK and P.V loops below: called after each step's MFMAs with
+// the step's index (a compile-time value once the loop is unrolled), so that
+// a caller can spread other instructions (tile transfers) over the MFMA
+// loop.  The default does nothing.
 struct NoHook {
     __device__ __forceinline__ void operator()(int) const {}
 };
@@ -499,9 +500,9 @@ __device__ __forceinline__ void prefill_qk(const char *kl, const Cols<D> (&cols)
 // ascending from zero), walked with the head-dim step outermost; the K
 // fragments are read through a ring of RD register sets, each reloaded
 // with the fragment RD positions ahead as soon as its MFMA is issued.
-template <int D, int CB, int RD = 6>
+template <int D, int CB, int RD = 6, class Hook = NoHook>
 __device__ __forceinline__ void prefill_qk_wide(const char *kl, const Cols<D> (&cols)[CB],
-                                                f32x4 (&s)[CB][Geo<D>::NKB])
+                                                f32x4 (&s)[CB][Geo<D>::NKB], Hook hook = Hook{})
 {
     using G = Geo<D>;
     const int lane = threadIdx.x & 63;
@@ -541,6 +542,7 @@ __device__ __forceinline__ void prefill_qk_wide(const char *kl, const Cols<D> (&
         if (j + RD < N)
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_barrier(0);
+        hook(j);
     }
 }
 
@@ -663,9 +665,9 @@ __device__ __forceinline__ void prefill_softmax(f32x4 (&s)[CB][Geo<D>::NKB], con
 // waves that have their SIMD to themselves): per block the same chain (32-key
 // steps ascending from zero) and the same fold fma(tile, h, ACC) as
 // prefill_pv.
-template <int D, int CB, int DG, bool RS = false>
+template <int D, int CB, int DG, bool RS = false, class Hook = NoHook>
 __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf)[CB][Geo<D>::NKS],
-                                               const FoldF (&f)[CB], State<D> (&st)[CB])
+                                               const FoldF (&f)[CB], State<D> (&st)[CB], Hook hook = Hook{})
 {
     using G = Geo<D>;
     static_assert(G::NDB % DG == 0, "whole groups");
@@ -706,6 +708,7 @@ __device__ __forceinline__ void prefill_pv_grp(const char *vl, const bf16x8 (&pf
                 __builtin_amdgcn_sched_group_barrier(0x100, DG, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, DG * CB, 0);
             __builtin_amdgcn_sched_barrier(0);
+            hook((db0 / DG) * G::NKS + stp);
         }
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
@@ -1599,12 +1602,14 @@ __device__ __forceinline__ void id_dma(const int32_t *src, int npages, uint32_t 
 
 // Workgroup = (column group, kv head, sequence): NWV waves x CB column
 // blocks.  One LDS buffer for the K tile and one for the V tile, each
-// refilled straight from HBM as soon as its last reader is done: K(t+1) is in
-// flight during the softmax and P.V of tile t, V(t+1) during QK and the
-// softmax of tile t+1.  The tile's 1 KB chunks are split evenly over the
-// waves; wave 0 fetches the block ids of tile t+2 (to LDS) with tile t+1's V.
-// Per column the arithmetic is exactly the tile step of the other prefill
-// kernels.
+// refilled straight from HBM as soon as its last reader is done: each wave
+// copies its share of V(t) during QK(t) and of K(t+1) during the first half
+// of P.V(t), one 1 KB chunk at a time between MFMAs (a wave waits while the
+// CU's memory pipeline takes its transfer instructions, so the copies are
+// spread rather than issued together between the phases).  V(t) lands during
+// the softmax, K(t+1) during the rest of P.V; wave 0 fetches the block ids of
+// tile t+2 (to LDS) after P.V(t).  Per column the arithmetic is exactly the
+// tile step of the other prefill kernels.
 template <int D, int CB, int NWV, int WPE>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void prefill_sb_kernel(AttnArgs a)
 {
@@ -1676,59 +1681,116 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             db_chunks4(src + part * 1024, is_k ? o.k : o.v, lds_addr(buf + page * G::PAGE + part * 1024));
         }
     };
+    // This wave's chunks of a K (or V) tile in runs of four (one source base
+    // and one M0 value per run), issued one chunk at a time from the hooks of
+    // the MFMA loops.
+    constexpr int NR = CPW / 4;
+    static_assert(CPW <= CPP && CPP % CPW == 0, "a wave's chunks lie in one page");
+    struct Runs {
+        const char *base[NR];
+        uint32_t m0[NR], off;
+    };
+    auto runs = [&](bool is_k, int tile) {
+        Runs r;
+        char *const buf = is_k ? kbuf : vbuf;
+        const uint16_t *const cache = is_k ? a.k_cache : a.v_cache;
+        const int64_t stride = is_k ? a.k_block_stride : a.v_block_stride;
+        const uint32_t nb = a.num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)a.num_blocks;
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+            const int ch = wave * CPW + 4 * q;
+            const int page = ch / CPP, part = ch % CPP;
+            int id = __builtin_amdgcn_readfirstlane(ids[(tile & 1) * G::NKB + page]);
+            id = (uint32_t)id < nb ? id : 0;
+            r.base[q] = reinterpret_cast<const char *>(cache + (int64_t)id * stride + (int64_t)kvh * BS * D) + part * 1024;
+            r.m0[q] = lds_addr(buf + page * G::PAGE + part * 1024);
+        }
+        const DbOffsets o = db_offsets(wave * CPW / CPP);
+        r.off = is_k ? o.k : o.v;
+        return r;
+    };
+    auto chunk = [&](const Runs &r, int c) {
+        const int q = c / 4, i = c % 4;
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%2"
+                     :
+                     : "v"(r.off), "s"(r.base[q]), "i"(i * 1024), "{m0}"(r.m0[q]));
+    };
     auto fetch_ids = [&](int tile) {
         if (wave == 0)
             id_dma(bt_row + tile * G::NKB, G::NKB, lds_addr(ids + (tile & 1) * G::NKB));
     };
 
-    // ---- prologue: ids of tile 0, then K(0), V(0) and the ids of tile 1
+    // ---- prologue: ids of tile 0, then K(0) and the ids of tile 1
     fetch_ids(0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     issue(true, 0);
-    issue(false, 0);
     if (last >= 1)
         fetch_ids(1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    // Per tile: V(t) is copied during QK(t) (one chunk per NQ MFMAs) and
+    // K(t+1) during the first half of P.V(t), so the copies land during the
+    // softmax (resp. the rest of P.V) and no wave waits on the memory
+    // pipeline between the phases.
+    constexpr int NQ = G::NDS * G::NKB / CPW;                 // QK MFMAs per chunk
+    constexpr int NPV = G::NDB / 2 * G::NKS;                  // P.V hook calls (two dim blocks per group)
+    static_assert(NQ >= 1 && NPV >= 2 * CPW, "chunks fit the loops");
     for (int t = 0; t <= last; ++t) {
         f32x4 sc[CB][G::NKB];
         bf16x8 pf[CB][G::NKS];
         FoldF f[CB];
-        if (active)
-            prefill_qk_wide<D, CB, 4>(kbuf, cols, sc);      // a shallow ring: registers are scarce here
+        {
+            const Runs rv = runs(false, t);
+            if (active) {
+                prefill_qk_wide<D, CB, 4>(kbuf, cols, sc, [&](int j) {
+                    if (j % NQ == NQ - 1)
+                        chunk(rv, j / NQ);
+                });
+            } else {
+#pragma unroll
+                for (int c = 0; c < CPW; ++c)
+                    chunk(rv, c);
+            }
+        }
         __syncthreads();                                   // K(t) read by every wave
-        if (t < last)
-            issue(true, t + 1);
         if (active) {
             if ((t + 1) * G::T > min_lim)
                 prefill_softmax<D, CB, true>(sc, cols, t, a.scale_log2, st, pf, f);
             else
                 prefill_softmax<D, CB, false>(sc, cols, t, a.scale_log2, st, pf, f);
         }
-        // V(t) (issued before K(t+1)) has landed
-        if (t < last)
-            wait_vm<CPW>();
-        else
-            wait_vm<0>();
+        __builtin_amdgcn_s_waitcnt(0);                     // V(t) landed
         __syncthreads();
         if ((t + 1) * G::T > seq_len) {
             db_mask_tail<D, NWV>(vbuf, seq_len, t);
             __syncthreads();
         }
-        if (active)
-            prefill_pv_grp<D, CB, 2>(vbuf, pf, f, st);      // two dim blocks at a time: registers are scarce
+        {
+            // K(t+1); past the last tile a spare copy (the slot's ids are
+            // stale but sanitised) into kbuf, which no wave reads after QK(t)
+            const Runs rk = runs(true, t + 1);
+            if (active) {
+                prefill_pv_grp<D, CB, 2>(vbuf, pf, f, st, [&](int k) {
+                    if (k % 2 == 0 && k / 2 < CPW)
+                        chunk(rk, k / 2);
+                });
+            } else {
+#pragma unroll
+                for (int c = 0; c < CPW; ++c)
+                    chunk(rk, c);
+            }
+        }
         __syncthreads();                                   // V(t) read by every wave
         if (t < last) {
             if (t + 2 <= last)
-                fetch_ids(t + 2);
-            issue(false, t + 1);
-            // K(t+1) and the ids of t+2 (issued before V(t+1)) have landed
-            wait_vm<CPW>();
+                fetch_ids(t + 2);                          // its slot held the ids of tile t
+            __builtin_amdgcn_s_waitcnt(0);                 // K(t+1) and the ids of t+2 landed
             __syncthreads();
         }
     }
+    __builtin_amdgcn_s_waitcnt(0);                         // the spare K copy
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const ColInfo cj = col_info(a, cg * NCOL + (wave * CB + cb) * 16 + c, kvh, q0, q_len, seq_len);

@@ -628,6 +628,46 @@ def test_prefill_kernel_per_grid_size(lens, Hq, Hkv, D, ncol):
     bitwise(g.run(), full[w.query_start_loc[1:] - 1], "decode vs prefill last rows (%s, D=%d)" % (lens, D))
 
 
+@pytest.mark.parametrize("lens,Hq,Hkv,D,ncol", [
+    ([600, 550, 500], 8, 1, 128, 64),               # 3 rows, producer / consumer kernel
+    ([1500], 24, 3, 128, 128),                      # 3 rows, double-buffered kernel
+    ([1700], 40, 5, 128, 256),                      # 5 rows, ping-pong kernel
+    ([300, 280, 260, 240, 220], 4, 1, 256, 64),     # 5 rows, producer / consumer kernel, head_dim 256
+    ([1400, 1400, 1400], 8, 1, 512, 128),           # 3 rows, single-buffer kernel
+    ([700, 600, 500], 8, 1, 512, 64),               # 3 rows, wave-pair kernel
+    ([500, 470, 440, 410, 380, 350], 8, 1, 128, 64),   # 6 rows, producer / consumer kernel
+], ids=["ss128_3", "db128_3", "pp_5", "ss256_5", "sb512_3", "ws512_3", "ss128_6"])
+def test_prefill_workgroup_mapping_covers_every_row(lens, Hq, Hkv, D, ncol):
+    """Grids whose rows (sequence x kv head) have more column groups than one
+    XCD's share of the grid deal the (row, column group) pairs out over the
+    XCDs one by one; with row counts that do not divide 8 an XCD cycles
+    through the rows.  Every output row must be written exactly as the
+    oracle says: no row left at the NaN fill, sampled rows against the
+    oracle, decode against the prefill's last rows, and a reordered batch
+    (every workgroup computes a different pair) bitwise equal per sequence."""
+    w = wl.random_case(311 + D + len(lens) + Hkv, lens, lens, Hq, Hkv, D)
+    G = Hq // Hkv
+    cgs = -(-int(w.max_query_len) * G // ncol)
+    rows_n = w.batch * Hkv
+    assert rows_n % 8 != 0 and cgs > -(-rows_n * cgs // 8), "the case must take the dealt-out mapping"
+    g, full, _ = _run_and_compare(w, rows=_rows(group_rows(w, 8, groups=("first", "last")), sample_rows(w, 40)),
+                                  what="mapping %s Hkv=%d D=%d" % (lens, Hkv, D))
+    assert kvp.kvp_get_counters()["last_grid_blocks"] == -(-(rows_n * cgs) // 8) * 8
+    assert not np.isnan(bf16_to_f32(full)).any(), "some output row was never written"
+    d = w.decode_view()
+    g.set_queries(d.q, d.query_lens)
+    bitwise(g.run(), full[w.query_start_loc[1:] - 1], "mapping: decode vs prefill last rows")
+    if w.batch > 1:
+        order = list(range(w.batch))[::-1]
+        qsl = w.query_start_loc
+        q = np.concatenate([w.q[qsl[b]:qsl[b + 1]] for b in order])
+        g.set_queries(q, [int(w.query_lens[b]) for b in order], block_tables=w.block_tables[order],
+                      seq_lens=w.seq_lens[order])
+        rev = g.run()
+        exp = np.concatenate([full[qsl[b]:qsl[b + 1]] for b in order])
+        bitwise(rev, exp, "mapping: reversed batch")
+
+
 def _random_shape(rng):
     D = int(rng.choice([128, 256, 512]))
     Hkv = int(rng.choice([1, 2, 4]))

@@ -1608,8 +1608,10 @@ __device__ __forceinline__ void id_dma(const int32_t *src, int npages, uint32_t 
 // CU's memory pipeline takes its transfer instructions, so the copies are
 // spread rather than issued together between the phases).  V(t) lands during
 // the softmax, K(t+1) during the rest of P.V; wave 0 fetches the block ids of
-// tile t+2 (to LDS) after P.V(t).  Per column the arithmetic is exactly the
-// tile step of the other prefill kernels.
+// tile t+2 (to LDS) during P.V(t).  Two barriers per tile; between the QK and
+// the softmax there is none, so a SIMD's first wave starts its softmax while
+// the second still runs its QK MFMAs.  Per column the arithmetic is exactly
+// the tile step of the other prefill kernels.
 template <int D, int CB, int NWV, int WPE>
 __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void prefill_sb_kernel(AttnArgs a)
 {
@@ -1737,6 +1739,9 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     constexpr int NQ = G::NDS * G::NKB / CPW;                 // QK MFMAs per chunk
     constexpr int NPV = G::NDB / 2 * G::NKS;                  // P.V hook calls (two dim blocks per group)
     static_assert(NQ >= 1 && NPV >= 2 * CPW, "chunks fit the loops");
+    // Two barriers per tile: after the softmax (every wave's V(t) chunks
+    // have landed and every wave has read K(t)) and at the end (every wave
+    // has read V(t); K(t+1) and the ids of tile t+2 have landed).
     for (int t = 0; t <= last; ++t) {
         f32x4 sc[CB][G::NKB];
         bf16x8 pf[CB][G::NKS];
@@ -1754,19 +1759,20 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
                     chunk(rv, c);
             }
         }
-        __syncthreads();                                   // K(t) read by every wave
         if (active) {
             if ((t + 1) * G::T > min_lim)
                 prefill_softmax<D, CB, true>(sc, cols, t, a.scale_log2, st, pf, f);
             else
                 prefill_softmax<D, CB, false>(sc, cols, t, a.scale_log2, st, pf, f);
         }
-        __builtin_amdgcn_s_waitcnt(0);                     // V(t) landed
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0);                     // this wave's V(t) chunks landed
+        __syncthreads();                                   // V(t) whole; K(t) read by every wave
         if ((t + 1) * G::T > seq_len) {
             db_mask_tail<D, NWV>(vbuf, seq_len, t);
             __syncthreads();
         }
+        if (t + 2 <= last)
+            fetch_ids(t + 2);                              // its slot held the ids of tile t
         {
             // K(t+1); past the last tile a spare copy (the slot's ids are
             // stale but sanitised) into kbuf, which no wave reads after QK(t)
@@ -1782,15 +1788,9 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
                     chunk(rk, c);
             }
         }
-        __syncthreads();                                   // V(t) read by every wave
-        if (t < last) {
-            if (t + 2 <= last)
-                fetch_ids(t + 2);                          // its slot held the ids of tile t
-            __builtin_amdgcn_s_waitcnt(0);                 // K(t+1) and the ids of t+2 landed
-            __syncthreads();
-        }
+        __builtin_amdgcn_s_waitcnt(0);                     // K(t+1) and the ids of t+2 landed
+        __syncthreads();                                   // and V(t) read by every wave
     }
-    __builtin_amdgcn_s_waitcnt(0);                         // the spare K copy
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const ColInfo cj = col_info(a, cg * NCOL + (wave * CB + cb) * 16 + c, kvh, q0, q_len, seq_len);

@@ -1600,6 +1600,60 @@ __device__ __forceinline__ void id_dma(const int32_t *src, int npages, uint32_t 
                      : "memory");
 }
 
+// P.V of one 16-column block with the V fragments read through a ring of
+// RD register sets (the single-buffer kernel's form: its registers leave no
+// room for two dim blocks in flight): per 16-dim block the same chain
+// (32-key steps ascending from zero) and the same fold fma(tile, h, ACC) as
+// prefill_pv.  Each ring slot is reloaded with the fragment RD positions
+// ahead as soon as its MFMA is issued, and a block is folded while the next
+// block's MFMAs run.
+template <int D, int RD, class Hook = NoHook>
+__device__ __forceinline__ void prefill_pv_ring(const char *vl, const bf16x8 (&pf)[Geo<D>::NKS], const FoldF &f,
+                                                State<D> &st, Hook hook = Hook{})
+{
+    using G = Geo<D>;
+    constexpr int N = G::NDB * G::NKS;           // fragment j: dim block j / NKS, key step j % NKS
+    static_assert(RD >= 1 && RD <= N, "ring depth");
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    // the lane's operand of dim block db lies (db / 2) KB + (db % 2) * 256 B
+    // past its operand of block 0 (vslot of dim 16 db + c)
+    const char *const vb = vl + (g >> 1) * G::PAGE + vslot(c, g & 1) * 16;
+    auto frag = [&](int j) {
+        const int db = j / G::NKS, stp = j % G::NKS;
+        return *reinterpret_cast<const bf16x8 *>(vb + (db >> 1) * 1024 + (db & 1) * 256 + 2 * stp * G::PAGE);
+    };
+    bf16x8 ring[RD];
+#pragma unroll
+    for (int j = 0; j < RD; ++j)
+        ring[j] = frag(j);
+    f32x4 o, prev;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const int db = j / G::NKS, stp = j % G::NKS;
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[j % RD], pf[stp], stp == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : o,
+                                                    0, 0, 0);
+        if (j + RD < N)
+            ring[j % RD] = frag(j + RD);
+        if (stp == G::NKS - 1) {
+            if (db > 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st.acc[db - 1][i] = __builtin_fmaf(prev[i], f.h, st.acc[db - 1][i]);
+            }
+            prev = o;
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (j + RD < N)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        hook(j);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        st.acc[G::NDB - 1][i] = __builtin_fmaf(prev[i], f.h, st.acc[G::NDB - 1][i]);
+}
+
 // Workgroup = (column group, kv head, sequence): NWV waves x CB column
 // blocks.  One LDS buffer for the K tile and one for the V tile, each
 // refilled straight from HBM as soon as its last reader is done: each wave
@@ -1737,8 +1791,8 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
     // softmax (resp. the rest of P.V) and no wave waits on the memory
     // pipeline between the phases.
     constexpr int NQ = G::NDS * G::NKB / CPW;                 // QK MFMAs per chunk
-    constexpr int NPV = G::NDB / 2 * G::NKS;                  // P.V hook calls (two dim blocks per group)
-    static_assert(NQ >= 1 && NPV >= 2 * CPW, "chunks fit the loops");
+    static_assert(CB == 1, "one column block per wave (P.V through a fragment ring)");
+    static_assert(NQ >= 1 && G::NDB * G::NKS >= 4 * CPW, "chunks fit the loops");
     // Two barriers per tile: after the softmax (every wave's V(t) chunks
     // have landed and every wave has read K(t)) and at the end (every wave
     // has read V(t); K(t+1) and the ids of tile t+2 have landed).
@@ -1778,9 +1832,9 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(WPE, W
             // stale but sanitised) into kbuf, which no wave reads after QK(t)
             const Runs rk = runs(true, t + 1);
             if (active) {
-                prefill_pv_grp<D, CB, 2>(vbuf, pf, f, st, [&](int k) {
-                    if (k % 2 == 0 && k / 2 < CPW)
-                        chunk(rk, k / 2);
+                prefill_pv_ring<D, 3>(vbuf, pf[0], f[0], st[0], [&](int j) {
+                    if (j % 4 == 0 && j / 4 < CPW)
+                        chunk(rk, j / 4);
                 });
             } else {
 #pragma unroll

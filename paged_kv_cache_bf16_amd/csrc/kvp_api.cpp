@@ -56,6 +56,36 @@ int64_t page_elems(const kvp_pool_desc &d) { return (int64_t)d.num_kv_heads * KV
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Whether some K page and some V page of the pool share an element (each
+// page is pg elements; K page i starts at element i * k_block_stride of
+// k_cache, V page j at j * v_block_stride of v_cache; the pointers are
+// 16-byte aligned, so their distance is a whole number of elements).
+bool kv_pages_overlap(const kvp_pool_desc &d, int64_t pg)
+{
+    const int64_t n = d.num_blocks, sk = d.k_block_stride, sv = d.v_block_stride;
+    const int64_t x0 = ((const char *)d.v_cache - (const char *)d.k_cache) / 2;   // V page 0, in K elements
+    // spans apart: no page of one reaches the other
+    if (x0 >= (n - 1) * sk + pg || x0 + (n - 1) * sv + pg <= 0)
+        return false;
+    if (sk == sv) {
+        // two lattices of one step: apart iff every V page sits in a gap
+        int64_t r = x0 % sk;
+        if (r < 0)
+            r += sk;
+        return r < pg || sk - r < pg;
+    }
+    // V page j starting at K element x meets K page i iff x - pg < i * sk <
+    // x + pg; with sk >= pg only i = floor(x / sk) and the next one can
+    for (int64_t j = 0; j < n; ++j) {
+        const int64_t x = x0 + j * sv;
+        const int64_t i0 = x >= 0 ? x / sk : -((-x + sk - 1) / sk);
+        for (int64_t i = i0; i <= i0 + 1; ++i)
+            if (i >= 0 && i < n && x - i * sk < pg && i * sk - x < pg)
+                return true;
+    }
+    return false;
+}
+
 // ---- reshape_and_cache: checks (nothing submitted) and launch
 int prepare_cache(const kvp_pool *pool, const void *k, const void *v, int64_t num_tokens, int64_t k_token_stride,
                   int64_t v_token_stride, const int64_t *slot_mapping, kvp::CacheArgs &a)
@@ -313,18 +343,8 @@ int kv_pool_create(const kvp_pool_desc *desc, kvp_pool **out)
         return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: block strides must be >= %lld elements", (long long)pg);
     if (d.k_block_stride % 8 || d.v_block_stride % 8)
         return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: block strides must be multiples of 8 elements");
-    // K and V page sets of the same block index must not overlap, and with
-    // equal strides the two lattices must interleave without touching.
-    const int64_t diff = ((const char *)d.v_cache - (const char *)d.k_cache) / 2;
-    if (d.k_block_stride == d.v_block_stride) {
-        const int64_t s = d.k_block_stride;
-        int64_t r = diff % s;
-        if (r < 0)
-            r += s;
-        const bool far = diff >= d.num_blocks * s || -diff >= d.num_blocks * s;
-        if (!far && (r < pg || s - r < pg))
-            return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: K and V pages overlap");
-    }
+    if (kv_pages_overlap(d, pg))
+        return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: K and V pages overlap");
     kvp_pool *p = new (std::nothrow) kvp_pool;
     if (!p)
         return fail(KVP_ERR_INVALID_ARGUMENT, "kv_pool_create: out of host memory");

@@ -71,6 +71,37 @@ def test_pool_create_rejects(lib, kw, code):
     assert lib.kvp_last_error().decode()
 
 
+def test_pool_create_overlap_matches_brute_force(lib):
+    # K page i covers elements [i*sk, i*sk + pg) from k_cache, V page j
+    # [x0 + j*sv, x0 + j*sv + pg); creation must fail exactly when some pair
+    # shares an element (equal and unequal strides, V before or after K)
+    pg = 16 * 128                                  # one kv head, Dh 128
+    rng = np.random.default_rng(7)
+    seen = {True: 0, False: 0}
+    for trial in range(400):
+        n = int(rng.integers(1, 7))
+        sk = pg + 8 * int(rng.integers(0, 3 * pg // 8))
+        sv = sk if trial % 3 == 0 else pg + 8 * int(rng.integers(0, 3 * pg // 8))
+        x0 = 8 * int(rng.integers(-(n * max(sk, sv)) // 8 - pg // 8, (n * max(sk, sv)) // 8 + pg // 8))
+        overlap = any(x0 + j * sv < i * sk + pg and i * sk < x0 + j * sv + pg for i in range(n) for j in range(n))
+        rc, h = create(lib, num_blocks=n, num_kv_heads=1, k_block_stride=sk, v_block_stride=sv,
+                       v_cache=FAKE_K + 2 * x0)
+        assert rc == (kvp.KVP_ERR_INVALID_ARGUMENT if overlap else 0), (n, sk, sv, x0, lib.kvp_last_error())
+        if rc == 0:
+            lib.kv_pool_destroy(h)
+        seen[overlap] += 1
+    assert seen[True] > 50 and seen[False] > 50
+    # unequal strides interleaved without touching: K pages at 2i*pg, V pages at (4j+1)*pg
+    rc, h = create(lib, num_blocks=1000, num_kv_heads=1, k_block_stride=2 * pg, v_block_stride=4 * pg,
+                   v_cache=FAKE_K + 2 * pg)
+    assert rc == 0, lib.kvp_last_error()
+    lib.kv_pool_destroy(h)
+    # and with V page 0 on K page 1
+    rc, h = create(lib, num_blocks=1000, num_kv_heads=1, k_block_stride=2 * pg, v_block_stride=3 * pg,
+                   v_cache=FAKE_K + 4 * pg)
+    assert rc == kvp.KVP_ERR_INVALID_ARGUMENT
+
+
 def test_pool_create_interleaved_and_span(lib):
     page = 2 * 16 * 128
     rc, h = create(lib, v_cache=FAKE_K + 2 * page, k_block_stride=2 * page, v_block_stride=2 * page,

@@ -98,7 +98,9 @@ typedef struct kvp_pool kvp_pool;   /* opaque host-side descriptor */
  * ("ROCm: harden compact peer-local KV prefill for Gemma-4", Required
  * hardening: invalid metadata and byte budgets are covered before
  * submission).  *out receives the handle; the library reads `desc` only
- * during this call.
+ * during this call.  The K/V overlap check is constant-time when the two
+ * block strides are equal or the K and V spans are apart, and walks the
+ * blocks once otherwise.
  * Errors: INVALID_ARGUMENT (null, non-positive sizes, short strides,
  * misaligned pointers, overlapping K/V pages), UNSUPPORTED (head_dim,
  * block_size). */
